@@ -1,0 +1,362 @@
+// capi.cpp -- the C ABI (include/moe.h): host-side argument checks, plan
+// carving, workspace sizing and the launch sequence of moe_forward.  Every
+// check runs before anything is enqueued; nothing here allocates device
+// memory or synchronises the host.
+#include <float.h>
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "internal.h"
+
+using namespace moe;
+
+namespace {
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+// Plan layout inside a workspace: e2p, p2e, tile_expert, tile_limit,
+// num_tiles, offsets, counts, scratch -- each piece 256-byte aligned.
+struct PlanLayout {
+  size_t e2p, p2e, te, tl, nt, off, cnt, scratch, total;
+  int64_t slots;
+  int max_tiles, max_spans;
+};
+
+PlanLayout plan_layout(int M, int top_k, int El, int tile) {
+  PlanLayout L;
+  const int64_t R = (int64_t)M * top_k;
+  L.slots = moe_route_slots(M, top_k, El, tile);
+  L.max_tiles = (int)(L.slots / tile);
+  L.max_spans = sort_max_spans(R);
+  size_t o = 0;
+  L.e2p = o; o = align256(o + sizeof(int32_t) * (size_t)(R > 0 ? R : 1));
+  L.p2e = o; o = align256(o + sizeof(int32_t) * (size_t)(L.slots > 0 ? L.slots : 1));
+  L.te = o; o = align256(o + sizeof(int32_t) * (size_t)(L.max_tiles > 0 ? L.max_tiles : 1));
+  L.tl = o; o = align256(o + sizeof(int32_t) * (size_t)(L.max_tiles > 0 ? L.max_tiles : 1));
+  L.nt = o; o = align256(o + sizeof(int32_t));
+  L.off = o; o = align256(o + sizeof(int32_t) * (size_t)(El + 1));
+  L.cnt = o; o = align256(o + sizeof(int32_t) * (size_t)El);
+  L.scratch = o; o = align256(o + sizeof(int32_t) * (size_t)L.max_spans * El);
+  L.total = o;
+  return L;
+}
+
+bool plan_args_ok(int M, int top_k, int El, int tile) {
+  return M >= 0 && top_k >= 1 && top_k <= 64 && El >= 1 && El <= MAX_LOCAL_EXPERTS && pow2_in(tile, 16, 256);
+}
+
+moe_status_t dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+bool plan_ok(const moe_plan_t* p) {
+  return p && p->expanded_to_permuted && p->permuted_to_expanded && p->tile_to_expert && p->tile_to_mn_limit &&
+         p->num_tiles && p->expert_offsets && p->expert_counts && p->scratch &&
+         plan_args_ok(p->M, p->top_k, p->num_local_experts, p->tile) &&
+         p->route_slots == moe_route_slots(p->M, p->top_k, p->num_local_experts, p->tile);
+}
+
+bool mode_ok(int mode) { return mode == MOE_QUANT_W4A16 || mode == MOE_QUANT_W4A4 || mode == MOE_QUANT_MXFP8_MXFP4; }
+
+// shapes the kernels tile: H and I multiples of 128 (256 in the MX mode,
+// whose K step is 256)
+moe_status_t shape_check(int H, int I, int mode) {
+  if (H <= 0 || I <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  const int q = (mode == MOE_QUANT_MXFP8_MXFP4) ? 256 : 128;
+  if (H % q != 0 || I % q != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t y1_bytes(int mode, int64_t slots, int I) {
+  if (mode == MOE_QUANT_W4A16) return (size_t)slots * I * 2;
+  if (mode == MOE_QUANT_W4A4) return (size_t)slots * (I / 2);
+  return (size_t)slots * I;
+}
+size_t y1_sf_bytes(int mode, int64_t slots, int I) {
+  if (mode == MOE_QUANT_W4A16) return 0;
+  if (mode == MOE_QUANT_W4A4) return (size_t)slots * (I / 16);
+  return (size_t)slots * (I / 32);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or option (H and I must be multiples of 128, or of 256 in the MX mode; "
+                                     "tile a power of two in [16, 256]; at most 512 local experts)";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_DEVICE: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int64_t moe_route_slots(int M, int top_k, int num_local_experts, int tile) {
+  if (M < 0 || top_k < 1 || num_local_experts < 1 || tile < 1) return 0;
+  const int64_t R = (int64_t)M * top_k;
+  const int64_t busy = R < num_local_experts ? R : num_local_experts;
+  const int64_t need = R + busy * (tile - 1);
+  return (need + tile - 1) / tile * tile;
+}
+
+size_t moe_plan_workspace_size(int M, int top_k, int num_local_experts, int tile) {
+  if (!plan_args_ok(M, top_k, num_local_experts, tile)) return 0;
+  return plan_layout(M, top_k, num_local_experts, tile).total;
+}
+
+moe_status_t moe_plan_init(moe_plan_t* plan, void* workspace, size_t workspace_bytes, int M, int top_k,
+                           int num_local_experts, int tile) {
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (M < 0 || top_k < 1 || top_k > 64 || num_local_experts < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (num_local_experts > MAX_LOCAL_EXPERTS || !pow2_in(tile, 16, 256)) return MOE_ERR_UNSUPPORTED;
+  PlanLayout L = plan_layout(M, top_k, num_local_experts, tile);
+  if (!workspace || ((uintptr_t)workspace & 255) != 0 || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  uint8_t* b = (uint8_t*)workspace;
+  plan->expanded_to_permuted = (int32_t*)(b + L.e2p);
+  plan->permuted_to_expanded = (int32_t*)(b + L.p2e);
+  plan->tile_to_expert = (int32_t*)(b + L.te);
+  plan->tile_to_mn_limit = (int32_t*)(b + L.tl);
+  plan->num_tiles = (int32_t*)(b + L.nt);
+  plan->expert_offsets = (int32_t*)(b + L.off);
+  plan->expert_counts = (int32_t*)(b + L.cnt);
+  plan->scratch = (int32_t*)(b + L.scratch);
+  plan->route_slots = L.slots;
+  plan->max_tiles = L.max_tiles;
+  plan->tile = tile;
+  plan->M = M;
+  plan->top_k = top_k;
+  plan->num_local_experts = num_local_experts;
+  plan->max_spans = L.max_spans;
+  return MOE_OK;
+}
+
+moe_status_t moe_sort(const int32_t* topk_ids, int M, int top_k, int num_experts, int num_local_experts,
+                      int local_expert_offset, moe_route_order_t route_order, const moe_plan_t* plan,
+                      moe_stream_t stream) {
+  if (!plan_ok(plan)) return MOE_ERR_INVALID_ARGUMENT;
+  if (M != plan->M || top_k != plan->top_k || num_local_experts != plan->num_local_experts)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (M > 0 && !topk_ids) return MOE_ERR_INVALID_ARGUMENT;
+  if (local_expert_offset < 0 || num_experts < 1 || (int64_t)local_expert_offset + num_local_experts > num_experts)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (route_order != MOE_ROUTE_ORDER_AUTO && route_order != MOE_ROUTE_ORDER_SINGLE &&
+      route_order != MOE_ROUTE_ORDER_SPAN)
+    return MOE_ERR_INVALID_ARGUMENT;
+  return dev(launch_sort(topk_ids, M, top_k, local_expert_offset, route_order, plan, (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, const uint8_t* x_sf,
+                                      int64_t x_row_stride, const moe_plan_t* plan, const uint8_t* w1,
+                                      const uint8_t* w1_sf, const float* w1_alpha, int H, int I,
+                                      float swiglu_alpha, float swiglu_beta, float swiglu_limit,
+                                      const float* fc2_input_scale, void* y1, uint8_t* y1_sf,
+                                      moe_stream_t stream) {
+  if (!mode_ok(mode) || !plan_ok(plan)) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t s = shape_check(H, I, mode);
+  if (s != MOE_OK) return s;
+  if (!w1 || !w1_sf || !w1_alpha || !y1) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->M > 0 && !x) return MOE_ERR_INVALID_ARGUMENT;
+  if ((mode == MOE_QUANT_W4A16) != (x_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;   // x_sf None iff w4a16
+  if ((mode == MOE_QUANT_W4A4) != (fc2_input_scale != NULL)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((mode == MOE_QUANT_W4A16) != (y1_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t row_units = (mode == MOE_QUANT_W4A4) ? H / 2 : H;
+  if (x_row_stride != 0 && x_row_stride < row_units) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t stride = x_row_stride ? x_row_stride : row_units;
+  if ((stride * (mode == MOE_QUANT_W4A16 ? 2 : 1)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!(swiglu_limit > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
+  Gemm1Params p;
+  p.mode = mode;
+  p.x = x;
+  p.x_sf = x_sf;
+  p.x_row_stride = stride;
+  p.plan = plan;
+  p.w1 = w1;
+  p.w1_sf = w1_sf;
+  p.w1_alpha = w1_alpha;
+  p.H = H;
+  p.I = I;
+  p.swiglu_alpha = swiglu_alpha;
+  p.swiglu_beta = swiglu_beta;
+  p.swiglu_limit = swiglu_limit;
+  p.fc2_input_scale = fc2_input_scale;
+  p.y1 = y1;
+  p.y1_sf = y1_sf;
+  if (plan->M == 0) return MOE_OK;
+  return dev(launch_gemm1(p, (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint8_t* y1_sf,
+                               const moe_plan_t* plan, const uint8_t* w2, const uint8_t* w2_sf,
+                               const float* w2_alpha, int H, int I, uint16_t* y2, const float* topk_weights,
+                               float routed_scaling_factor, uint16_t* out, moe_stream_t stream) {
+  if (!mode_ok(mode) || !plan_ok(plan)) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t s = shape_check(H, I, mode);
+  if (s != MOE_OK) return s;
+  if (!y1 || !w2 || !w2_sf || !w2_alpha) return MOE_ERR_INVALID_ARGUMENT;
+  if ((mode == MOE_QUANT_W4A16) != (y1_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((y2 == NULL) == (out == NULL)) return MOE_ERR_INVALID_ARGUMENT;  // exactly one finalize mode
+  if (out && !topk_weights) return MOE_ERR_INVALID_ARGUMENT;
+  Gemm2Params p;
+  p.mode = mode;
+  p.y1 = y1;
+  p.y1_sf = y1_sf;
+  p.plan = plan;
+  p.w2 = w2;
+  p.w2_sf = w2_sf;
+  p.w2_alpha = w2_alpha;
+  p.H = H;
+  p.I = I;
+  p.y2 = y2;
+  p.topk_weights = topk_weights;
+  p.routed_scaling_factor = routed_scaling_factor;
+  p.out = out;
+  if (plan->M == 0) return MOE_OK;
+  return dev(launch_gemm2(p, (hipStream_t)stream));
+}
+
+moe_status_t moe_finalize(const uint16_t* y2, const moe_plan_t* plan, const float* topk_weights, int H,
+                          float routed_scaling_factor, int accumulate, uint16_t* out, moe_stream_t stream) {
+  if (!plan_ok(plan) || H <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (plan->M > 0 && (!y2 || !topk_weights || !out)) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->M == 0) return MOE_OK;
+  return dev(launch_finalize(y2, plan->expanded_to_permuted, topk_weights, plan->M, plan->top_k, H,
+                             routed_scaling_factor, accumulate ? 1 : 0, out, (hipStream_t)stream));
+}
+
+void moe_opts_init(moe_opts_t* o) {
+  if (!o) return;
+  memset(o, 0, sizeof(*o));
+  o->swiglu_alpha = 1.0f;
+  o->swiglu_beta = 0.0f;
+  o->swiglu_limit = FLT_MAX;
+  o->fc2_input_scale = NULL;
+  o->routed_scaling_factor = 1.0f;
+  o->accumulate = 0;
+  o->finalize_mode = MOE_FINALIZE_DETERMINISTIC;
+  o->route_order = MOE_ROUTE_ORDER_AUTO;
+  o->tile = 0;
+  o->x_row_stride = 0;
+}
+
+int moe_default_tile(int M, int top_k, int num_local_experts, moe_quant_mode_t mode) {
+  (void)mode;
+  const int64_t per_expert = (int64_t)M * top_k / (num_local_experts > 0 ? num_local_experts : 1);
+  if (per_expert <= 16) return 16;
+  if (per_expert <= 64) return 32;
+  return 64;
+}
+
+size_t moe_workspace_size(int M, int H, int I, int top_k, int num_local_experts, int tile, moe_quant_mode_t mode,
+                          int finalize_mode) {
+  if (!plan_args_ok(M, top_k, num_local_experts, tile) || !mode_ok(mode) || H <= 0 || I <= 0) return 0;
+  PlanLayout L = plan_layout(M, top_k, num_local_experts, tile);
+  size_t total = L.total;
+  total = align256(total + y1_bytes(mode, L.slots, I));
+  total = align256(total + y1_sf_bytes(mode, L.slots, I));
+  if (finalize_mode == MOE_FINALIZE_DETERMINISTIC) total = align256(total + (size_t)L.slots * H * 2);
+  return total;
+}
+
+moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk_ids, const float* topk_weights,
+                         const uint8_t* w1, const uint8_t* w1_sf, const float* w1_alpha, const uint8_t* w2,
+                         const uint8_t* w2_sf, const float* w2_alpha, int num_experts, int top_k,
+                         int num_local_experts, int local_expert_offset, moe_quant_mode_t quant_mode,
+                         uint16_t* out, int M, int H, int I, const moe_opts_t* opts, moe_stream_t stream) {
+  if (!opts || !mode_ok(quant_mode)) return MOE_ERR_INVALID_ARGUMENT;
+  if (M < 0 || top_k < 1 || top_k > 64 || num_local_experts < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (local_expert_offset < 0 || (int64_t)local_expert_offset + num_local_experts > num_experts)
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t s = shape_check(H, I, quant_mode);
+  if (s != MOE_OK) return s;
+  if (opts->finalize_mode != MOE_FINALIZE_DETERMINISTIC && opts->finalize_mode != MOE_FINALIZE_ATOMIC)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (M > 0 && (!x || !topk_ids || !topk_weights || !out)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!w1 || !w1_sf || !w1_alpha || !w2 || !w2_sf || !w2_alpha) return MOE_ERR_INVALID_ARGUMENT;
+  if ((quant_mode == MOE_QUANT_W4A16) != (x_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((quant_mode == MOE_QUANT_W4A4) != (opts->fc2_input_scale != NULL)) return MOE_ERR_INVALID_ARGUMENT;
+  if (num_local_experts > MAX_LOCAL_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  const int tile = opts->tile ? opts->tile : moe_default_tile(M, top_k, num_local_experts, quant_mode);
+  if (!pow2_in(tile, 16, 256)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe_workspace_size(M, H, I, top_k, num_local_experts, tile, quant_mode, opts->finalize_mode);
+  if (!opts->workspace || opts->workspace_bytes < need || ((uintptr_t)opts->workspace & 255) != 0)
+    return MOE_ERR_WORKSPACE;
+
+  moe_plan_t plan;
+  PlanLayout L = plan_layout(M, top_k, num_local_experts, tile);
+  s = moe_plan_init(&plan, opts->workspace, L.total, M, top_k, num_local_experts, tile);
+  if (s != MOE_OK) return s;
+  uint8_t* base = (uint8_t*)opts->workspace + L.total;
+  void* y1 = base;
+  base += align256(y1_bytes(quant_mode, L.slots, I));
+  uint8_t* y1_sf = (quant_mode == MOE_QUANT_W4A16) ? NULL : base;
+  base += align256(y1_sf_bytes(quant_mode, L.slots, I));
+  uint16_t* y2 = (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC) ? (uint16_t*)base : NULL;
+
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = (hipEvent_t*)opts->phase_events;
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], st) : hipSuccess; };
+  if (mark(0) != hipSuccess) return MOE_ERR_DEVICE;
+  if (M == 0) {
+    if (!opts->accumulate && out) { /* nothing to write: M == 0 */ }
+    for (int i = 1; i < MOE_NUM_PHASE_EVENTS; i++)
+      if (mark(i) != hipSuccess) return MOE_ERR_DEVICE;
+    return MOE_OK;
+  }
+  s = moe_sort(topk_ids, M, top_k, num_experts, num_local_experts, local_expert_offset,
+               (moe_route_order_t)opts->route_order, &plan, stream);
+  if (s != MOE_OK) return s;
+  if (mark(1) != hipSuccess) return MOE_ERR_DEVICE;
+  if (opts->finalize_mode == MOE_FINALIZE_ATOMIC && !opts->accumulate) {
+    if (launch_zero_fill(out, (size_t)M * H * 2, st) != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  s = moe_grouped_gemm1_swiglu(quant_mode, x, x_sf, opts->x_row_stride, &plan, w1, w1_sf, w1_alpha, H, I,
+                               opts->swiglu_alpha, opts->swiglu_beta, opts->swiglu_limit, opts->fc2_input_scale, y1,
+                               y1_sf, stream);
+  if (s != MOE_OK) return s;
+  if (mark(2) != hipSuccess) return MOE_ERR_DEVICE;
+  if (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC) {
+    s = moe_grouped_gemm2(quant_mode, y1, y1_sf, &plan, w2, w2_sf, w2_alpha, H, I, y2, NULL,
+                          opts->routed_scaling_factor, NULL, stream);
+    if (s != MOE_OK) return s;
+    if (mark(3) != hipSuccess) return MOE_ERR_DEVICE;
+    s = moe_finalize(y2, &plan, topk_weights, H, opts->routed_scaling_factor, opts->accumulate, out, stream);
+    if (s != MOE_OK) return s;
+  } else {
+    s = moe_grouped_gemm2(quant_mode, y1, y1_sf, &plan, w2, w2_sf, w2_alpha, H, I, NULL, topk_weights,
+                          opts->routed_scaling_factor, out, stream);
+    if (s != MOE_OK) return s;
+    if (mark(3) != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  if (mark(4) != hipSuccess) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+moe_status_t moe_nvfp4_global_scale(const uint16_t* x, int64_t batches, int64_t batch_elems, float* gscale,
+                                    moe_stream_t stream) {
+  if (batches < 0 || batch_elems < 0 || (batches > 0 && (!x || !gscale))) return MOE_ERR_INVALID_ARGUMENT;
+  if (batch_elems % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (batches == 0) return MOE_OK;
+  return dev(launch_nvfp4_global_scale(x, batches, batch_elems, gscale, (hipStream_t)stream));
+}
+
+moe_status_t moe_quantize_nvfp4(const uint16_t* x, int64_t batches, int64_t rows, int64_t cols,
+                                const float* gscale, uint8_t* q, uint8_t* sf, moe_stream_t stream) {
+  if (batches < 0 || rows < 0 || cols < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (cols % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (batches * rows * cols > 0 && (!x || !gscale || !q || !sf)) return MOE_ERR_INVALID_ARGUMENT;
+  return dev(launch_quantize_nvfp4(x, batches, rows, cols, gscale, q, sf, (hipStream_t)stream));
+}
+
+moe_status_t moe_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int elem, uint8_t* q, uint8_t* sf,
+                             moe_stream_t stream) {
+  if (rows < 0 || cols < 0 || (elem != 0 && elem != 1)) return MOE_ERR_INVALID_ARGUMENT;
+  if (cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows * cols > 0 && (!x || !q || !sf)) return MOE_ERR_INVALID_ARGUMENT;
+  return dev(launch_quantize_mx(x, rows, cols, elem, q, sf, (hipStream_t)stream));
+}
+
+}  // extern "C"

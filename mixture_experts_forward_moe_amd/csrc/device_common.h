@@ -1,0 +1,131 @@
+// device_common.h -- gfx950 device helpers shared by the MoE kernels:
+// vector types, bf16 / E4M3 / E8M0 / E2M1 conversions on CDNA4 conversion
+// instructions, and the NVFP4 / MX block quantisers used by the GEMM1
+// epilogue and the input quantisers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define DEV __device__ __forceinline__
+
+DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+DEV uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// E4M3 ("fn") code -> fp32, exact.  Codes 0x7f/0xff (NaN) are not produced by
+// the quantisers and decode to 480 here.
+DEV float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// E8M0 code as the fp32 whose exponent field is the code: exactly 2^(c-127)
+// for c >= 1; c == 0 gives +0.0f, whose exponent field the CDNA4 scaled
+// conversions read as 2^-127.
+DEV float e8m0_scale_operand(uint32_t c) { return __uint_as_float(c << 23); }
+
+// Eight packed E2M1 codes (one dword, element 0 in the low nibble) times an
+// fp32 block scale, as eight bf16.  The product of an E2M1 value and an E4M3
+// value has at most 6 significant bits, so the result is exact.
+DEV bf16x8_t e2m1x8_scaled_to_bf16(uint32_t w, float scale) {
+  f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  u32x4_t r;
+  r[0] = pack_bf16x2(p0[0] * scale, p0[1] * scale);
+  r[1] = pack_bf16x2(p1[0] * scale, p1[1] * scale);
+  r[2] = pack_bf16x2(p2[0] * scale, p2[1] * scale);
+  r[3] = pack_bf16x2(p3[0] * scale, p3[1] * scale);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// fp32 -> E2M1 code (4 bits), round to nearest even, saturating to +-6; the
+// sign of a zero result follows the input.  Scale operand 1.0: no scaling.
+DEV uint32_t f32_to_e2m1(float v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 15u;
+}
+// two values -> one byte (a low nibble, b high nibble), divided by the
+// exponent of `scale` (a power of two or an E8M0 operand)
+DEV uint32_t f32x2_to_e2m1x2(float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, scale, 0) & 0xffu;
+}
+
+// fp32 -> E4M3 code, round to nearest even, saturating to +-448 (the
+// conversion itself does not saturate, so clamp first).
+DEV uint32_t f32_to_e4m3_sat(float v) {
+  v = fminf(fmaxf(v, -448.0f), 448.0f);
+  i16x2_t z = {0, 0};
+  i16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, v, 0.0f, 1.0f, false);
+  return (uint32_t)(uint16_t)r[0] & 0xffu;
+}
+
+// x / 2^(code-127) -> E4M3, saturating: clamp to +-448 * 2^(code-127) first
+DEV uint32_t f32x2_to_e4m3x2_mx(float a, float b, uint32_t code) {
+  float lim = __builtin_ldexpf(448.0f, (int)code - 127);
+  a = fminf(fmaxf(a, -lim), lim);
+  b = fminf(fmaxf(b, -lim), lim);
+  i16x2_t z = {0, 0};
+  i16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a, b, e8m0_scale_operand(code), false);
+  return (uint32_t)(uint16_t)r[0];
+}
+
+// NVFP4 block scale code for a block amax under global scale gs:
+// E4M3(bamax / (6 gs)) decided in fp32; 0 when either is 0.
+DEV uint32_t nvfp4_scale_code(float bamax, float gs) {
+  if (!(gs > 0.0f) || !(bamax > 0.0f)) return 0u;
+  float t = __fmul_rn(6.0f, gs);
+  float s = __fdiv_rn(bamax, t);
+  return f32_to_e4m3_sat(s);
+}
+
+// E2M1 code of v for a block with decoded scale sd under global scale gs:
+// E2M1(v / (sd * gs)) in fp32; 0 when sd * gs == 0.
+DEV uint32_t nvfp4_elem_code(float v, float sd, float gs) {
+  float denom = __fmul_rn(sd, gs);
+  if (!(denom > 0.0f)) return 0u;
+  return f32_to_e2m1(__fdiv_rn(v, denom));
+}
+
+// MX shared-exponent code for a block amax (OCP MX v1.0): floor(log2 amax) -
+// emax + 127 from the exponent bits, clamped to [0, 254]; 0 for amax == 0.
+DEV uint32_t mx_scale_code(float amax, int emax) {
+  int be = (int)((__float_as_uint(amax) >> 23) & 255u);
+  if (be == 0) return 0u;  // zero or subnormal amax: clamps to 0
+  int c = be - emax;
+  return (uint32_t)(c < 0 ? 0 : (c > 254 ? 254 : c));
+}
+
+DEV float warp_max16(float v) {
+  // max over the 16 lanes of a DPP row (lanes 16q .. 16q+15)
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
+// SwiGLU with alpha / beta / limit on fp32 gate and up values:
+// min(g, l) * sigmoid(a * min(g, l)) * (clamp(u, -l, l) + b)
+DEV float swiglu_f32(float g, float u, float alpha, float beta, float limit) {
+  float gc = fminf(g, limit);
+  float uc = fminf(fmaxf(u, -limit), limit);
+  float e = __expf(-alpha * gc);
+  float sig = __frcp_rn(1.0f + e);
+  return gc * sig * (uc + beta);
+}

@@ -1,0 +1,79 @@
+"""Helpers of the GPU parity tests: moving a quantised problem to the
+device, running the library's entry points, and the comparison bars."""
+import sys
+
+import numpy as np
+import torch
+
+import mixture_experts_forward_moe_amd as moe
+import oracle
+import synth
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray):
+    """numpy -> device tensor with the same bytes (uint16 bf16 bits -> int16)."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t, dtype=None):
+    a = t.cpu().numpy()
+    if dtype is not None:
+        a = a.view(dtype)
+    return a
+
+
+class DeviceProblem:
+    def __init__(self, p: oracle.Problem):
+        self.p = p
+        self.x = dev(p.x)
+        self.x_sf = dev(p.x_sf)
+        self.ids = dev(p.topk_ids)
+        self.w = dev(p.topk_weights)
+        self.w1, self.w1_sf, self.w1_alpha = dev(p.w1), dev(p.w1_sf), dev(p.w1_alpha)
+        self.w2, self.w2_sf, self.w2_alpha = dev(p.w2), dev(p.w2_sf), dev(p.w2_alpha)
+        self.fc2 = dev(np.array([p.fc2_input_scale], np.float32)) if p.mode == oracle.W4A4 else None
+
+    def forward(self, out=None, tile=0, **kw):
+        p = self.p
+        if out is None:
+            out = torch.zeros((p.M, p.H), dtype=torch.int16, device=DEV)
+        moe.moe_forward(self.x, self.x_sf, self.ids, self.w, self.w1, self.w1_sf, self.w1_alpha, self.w2,
+                        self.w2_sf, self.w2_alpha, p.num_experts, p.top_k, p.num_local_experts,
+                        p.local_expert_offset, p.mode, out, p.H, p.I, tile=tile,
+                        swiglu_alpha=p.swiglu_alpha, swiglu_beta=p.swiglu_beta, swiglu_limit=p.swiglu_limit,
+                        fc2_input_scale=self.fc2, routed_scaling_factor=p.routed_scaling_factor, **kw)
+        return out
+
+
+def bf16(bits):
+    return synth.bf16_to_f32(np.asarray(bits).view(np.uint16)).astype(np.float64)
+
+
+def check_close(got_bits, ref_bits, mode, what=""):
+    """The parity bar: rel-L2 <= 5e-3 and |err| <= 1e-2 max|ref| (W4A16, MX);
+    rel-L2 <= 2e-2 (W4A4 with its NVFP4 requantisation)."""
+    g = bf16(got_bits)
+    r = bf16(ref_bits)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    maxerr = np.abs(g - r).max() / max(np.abs(r).max(), 1e-30)
+    exact = float(np.mean(np.asarray(got_bits).view(np.uint16) == np.asarray(ref_bits).view(np.uint16)))
+    say(f"{what}: rel_l2={err:.3e} max_err/max_ref={maxerr:.3e} bit_exact_frac={exact:.4f}")
+    if mode == oracle.W4A4:
+        assert err <= 2e-2, (what, err)
+    else:
+        assert err <= 5e-3, (what, err)
+        assert maxerr <= 1e-2, (what, maxerr)
+    return err, maxerr, exact

@@ -1,0 +1,124 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/moe.h declares, and its host-side checks reject bad arguments with
+the documented status codes before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_forward_moe_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced by host checks
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = moe.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(moe.EXPORTS)
+
+
+def test_status_strings():
+    for s in range(5):
+        assert moe.status_string(s)
+
+
+def test_route_slots_formula():
+    assert moe.route_slots(16, 2, 8, 16) == 160
+    assert moe.route_slots(8, 8, 32, 16) == 544
+    assert moe.route_slots(4096, 8, 32, 64) == 34816
+    assert moe.route_slots(512, 8, 128, 32) == 8064
+    assert moe.route_slots(65536, 8, 32, 256) == 532480
+    assert moe.route_slots(0, 8, 32, 64) == 0
+
+
+def test_plan_init_checks():
+    L = moe.lib()
+    p = moe.Plan()
+    n = L.moe_plan_workspace_size(64, 8, 32, 16)
+    assert n > 0
+    assert L.moe_plan_init(ctypes.byref(p), FAKE, n, 64, 8, 32, 16) == OK
+    assert p.route_slots == moe.route_slots(64, 8, 32, 16) and p.max_tiles == p.route_slots // 16
+    assert L.moe_plan_init(ctypes.byref(p), FAKE, n - 1, 64, 8, 32, 16) == WORKSPACE
+    assert L.moe_plan_init(ctypes.byref(p), ctypes.c_void_p(0x10010), n, 64, 8, 32, 16) == WORKSPACE
+    assert L.moe_plan_init(ctypes.byref(p), FAKE, n, 64, 8, 32, 24) == UNSUPPORTED      # tile not a power of two
+    assert L.moe_plan_init(ctypes.byref(p), FAKE, n, 64, 8, 32, 512) == UNSUPPORTED
+    assert L.moe_plan_init(ctypes.byref(p), FAKE, n, 64, 0, 32, 16) == INVALID
+    assert L.moe_plan_init(None, FAKE, n, 64, 8, 32, 16) == INVALID
+
+
+def _plan(M=64, k=8, El=32, tile=16):
+    p = moe.Plan()
+    n = moe.lib().moe_plan_workspace_size(M, k, El, tile)
+    assert moe.lib().moe_plan_init(ctypes.byref(p), FAKE, n, M, k, El, tile) == OK
+    return p
+
+
+def test_sort_argument_checks():
+    L = moe.lib()
+    p = _plan()
+    assert L.moe_sort(FAKE, 64, 8, 256, 32, 240, 0, ctypes.byref(p), None) == INVALID   # offset + E_l > E
+    assert L.moe_sort(FAKE, 63, 8, 256, 32, 0, 0, ctypes.byref(p), None) == INVALID     # M differs from the plan
+    assert L.moe_sort(None, 64, 8, 256, 32, 0, 0, ctypes.byref(p), None) == INVALID
+    assert L.moe_sort(FAKE, 64, 8, 256, 32, 0, 7, ctypes.byref(p), None) == INVALID     # route order
+    assert L.moe_sort(FAKE, 64, 8, 256, 32, 0, 0, None, None) == INVALID
+
+
+def test_gemm_argument_checks():
+    L = moe.lib()
+    p = ctypes.byref(_plan())
+    g1 = L.moe_grouped_gemm1_swiglu
+    F = FAKE
+    # x_sf must be NULL exactly in W4A16; fc2_input_scale exactly in W4A4
+    assert g1(0, F, F, 0, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, None, F, None, None) == INVALID
+    assert g1(1, F, F, 0, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, None, F, F, None) == INVALID
+    assert g1(2, F, F, 0, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, F, F, F, None) == INVALID
+    assert g1(0, F, None, 0, p, F, F, F, 200, 512, 1.0, 0.0, 1e30, None, F, None, None) == UNSUPPORTED
+    assert g1(0, F, None, 0, p, F, F, F, 256, 96, 1.0, 0.0, 1e30, None, F, None, None) == UNSUPPORTED
+    assert g1(5, F, None, 0, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, None, F, None, None) == INVALID
+    assert g1(0, F, None, 100, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, None, F, None, None) == INVALID  # stride < H
+    g2 = L.moe_grouped_gemm2
+    assert g2(0, F, None, p, F, F, F, 256, 512, F, None, 1.0, F, None) == INVALID   # both y2 and out
+    assert g2(0, F, None, p, F, F, F, 256, 512, None, None, 1.0, None, None) == INVALID
+    assert g2(0, F, None, p, F, F, F, 256, 512, None, None, 1.0, F, None) == INVALID  # atomic needs weights
+    assert L.moe_finalize(F, p, F, 100, 1.0, 0, F, None) == UNSUPPORTED
+
+
+def test_forward_argument_checks():
+    L = moe.lib()
+    F = FAKE
+    o = moe.make_opts()
+    o.workspace = 0x10000
+    o.workspace_bytes = 16
+    args = lambda mode, xsf, M=16, H=256, I=512, El=8, off=0, E=8: (
+        F, xsf, F, F, F, F, F, F, F, F, E, 2, El, off, mode, F, M, H, I, ctypes.byref(o), None)
+    assert L.moe_forward(*args(0, None)) == WORKSPACE
+    assert L.moe_forward(*args(0, F)) == INVALID
+    assert L.moe_forward(*args(0, None, off=4)) == INVALID
+    assert L.moe_forward(*args(0, None, H=300)) == UNSUPPORTED
+    assert L.moe_forward(*args(1, F)) == INVALID                 # W4A4 needs fc2_input_scale
+    o.finalize_mode = 3
+    assert L.moe_forward(*args(0, None)) == INVALID
+    o.finalize_mode = 0
+    assert L.moe_forward(F, None, F, F, F, F, F, F, F, F, 8, 2, 8, 0, 0, F, 16, 256, 512, None, None) == INVALID
+
+
+def test_workspace_size_grows_with_mode():
+    a = moe.workspace_size(16, 256, 512, 2, 8, 16, 0, 0)
+    b = moe.workspace_size(16, 256, 512, 2, 8, 16, 0, 1)   # atomic: no y2
+    c = moe.workspace_size(16, 256, 512, 2, 8, 16, 1, 0)   # NVFP4 y1 is smaller than bf16
+    assert a > b > 0 and a > c > 0
+    assert moe.default_tile(8, 8, 32, 0) == 16
