@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE forward on one MI355X.
+
+One step = one moe_forward (sort, GEMM1 + SwiGLU, GEMM2, finalize) over one
+batch of seeded synthetic inputs already resident in HBM.  The headline
+workload is W4A16 decode (M=8 tokens, hidden 6144, inter 2048, 256 experts
+of which 32 are local, top_k 8), HBM-bound on weight bytes; the W4A16
+prefill workload (M=4096, biased router, SwiGLU limit 7), MFMA-bound, is
+reported alongside in the same line.  Weights, activations and routing are
+rotated over several resident copies so that no step finds the previous
+steps' weights in the 256 MB MALL.
+
+Prints ONE JSON line (rank 0, N=1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "fused-MoE fwd tokens/s + % HBM roofline (M=8) / % MFMA peak (M=4096)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ inputs
+class GpuInputs:
+    """One workload's inputs on the GPU, prepared with the library's own
+    quantisers from the seeded bf16 draws, in `copies` resident copies."""
+
+    def __init__(self, wl, copies: int):
+        import torch
+
+        import mixture_experts_forward_moe_amd as moe
+        import synth
+        self.wl = wl
+        E, H, I = wl.num_local_experts, wl.H, wl.I
+        raw = synth.make_raw(wl)
+        self.topk_ids_np = raw.topk_ids
+        dev = "cuda"
+        x = torch.from_numpy(raw.x.view(np.int16)).to(dev)
+        w1b = torch.from_numpy(raw.w1.view(np.int16)).to(dev)
+        w2b = torch.from_numpy(raw.w2.view(np.int16)).to(dev)
+        del raw
+        self.w1 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+        self.w1_sf = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=dev)
+        self.w2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
+        self.w2_sf = torch.empty((E, H, I // 16), dtype=torch.uint8, device=dev)
+        self.w1_alpha = torch.empty(E, dtype=torch.float32, device=dev)
+        self.w2_alpha = torch.empty(E, dtype=torch.float32, device=dev)
+        moe.moe_nvfp4_global_scale(w1b, E, self.w1_alpha)
+        moe.moe_quantize_nvfp4(w1b, E, 2 * I, H, self.w1_alpha, self.w1, self.w1_sf)
+        moe.moe_nvfp4_global_scale(w2b, E, self.w2_alpha)
+        moe.moe_quantize_nvfp4(w2b, E, H, I, self.w2_alpha, self.w2, self.w2_sf)
+        torch.cuda.synchronize()
+        del w1b, w2b
+        assert wl.mode == moe.W4A16, "the benchmark workloads are W4A16"
+        self.x = x
+        self.ids = torch.from_numpy(self.topk_ids_np).to(dev)
+        self.w = None
+        _, wts = synth.make_routing(wl)
+        self.w = torch.from_numpy(wts).to(dev)
+        # resident copies, rotated step by step
+        self.copies = [(self.x, self.ids, self.w, self.w1, self.w1_sf, self.w1_alpha, self.w2, self.w2_sf,
+                        self.w2_alpha)]
+        for _ in range(copies - 1):
+            self.copies.append(tuple(t.clone() for t in self.copies[0]))
+        torch.cuda.synchronize()
+
+    def local_stats(self):
+        wl = self.wl
+        ids = self.topk_ids_np
+        local = (ids >= wl.local_expert_offset) & (ids < wl.local_expert_offset + wl.num_local_experts)
+        routes = int(local.sum())
+        active = int(np.unique(ids[local]).size)
+        return routes, active
+
+
+def time_workload(wl, steps: int, warmup: int, copies: int):
+    """Times `steps` forwards twice on the same resident inputs: once bare
+    (the headline), once with HIP events recorded by moe_forward between its
+    launches on the same stream (per-kernel durations)."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    g = GpuInputs(wl, copies)
+    H, I, E = wl.H, wl.I, wl.num_local_experts
+    tile = moe.default_tile(wl.M, wl.top_k, E, wl.mode)
+    ws = torch.zeros(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.M, H), dtype=torch.int16, device="cuda")
+    nev = moe.NUM_PHASE_EVENTS
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    for row in events:          # torch creates an event on its first record
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    opts = [moe.make_opts(workspace=ws, tile=tile, swiglu_alpha=wl.swiglu_alpha, swiglu_beta=wl.swiglu_beta,
+                          swiglu_limit=wl.swiglu_limit)]
+    opts_ev = [moe.make_opts(workspace=ws, tile=tile, swiglu_alpha=wl.swiglu_alpha, swiglu_beta=wl.swiglu_beta,
+                             swiglu_limit=wl.swiglu_limit, phase_events=events[i]) for i in range(steps)]
+
+    def step(i, o):
+        x, ids, w, w1, w1s, w1a, w2, w2s, w2a = g.copies[i % len(g.copies)]
+        moe.moe_forward(x, None, ids, w, w1, w1s, w1a, w2, w2s, w2a, wl.num_experts, wl.top_k, E,
+                        wl.local_expert_offset, wl.mode, out, H, I, opts=o)
+
+    for i in range(warmup):
+        step(i, opts[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, opts[0])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    # the same steps with per-phase events
+    t1 = time.perf_counter()
+    for i in range(steps):
+        step(i, opts_ev[i])
+    torch.cuda.synchronize()
+    dt_ev = time.perf_counter() - t1
+    names = ["sort", "gemm1", "gemm2", "finalize"]
+    per = {n: float(np.mean([events[i][k].elapsed_time(events[i][k + 1]) for i in range(steps)]))
+           for k, n in enumerate(names)}
+    res = dict(seconds=dt, ms_per_step=dt * 1e3 / steps, ms_per_step_with_events=dt_ev * 1e3 / steps, tile=tile,
+               phase_ms=per)
+    routes, active = g.local_stats()
+    res["local_routes"] = routes
+    res["active_experts"] = active
+    del g
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ algorithmic work
+def w4a16_bytes(wl, routes, active):
+    """Algorithmic HBM bytes: active experts' NVFP4 weights (codes + E4M3
+    block scales), each token's bf16 row read once, y1/y2 written and read
+    once per local route, the output written once."""
+    H, I = wl.H, wl.I
+    w1 = 2 * I * H // 2 + 2 * I * H // 16
+    w2 = H * I // 2 + H * I // 16
+    return dict(
+        gemm1=active * w1 + routes * (H * 2 + I * 2),
+        gemm2=active * w2 + routes * (I * 2 + H * 2),
+        weights=active * (w1 + w2),
+        w1_per_expert=w1, w2_per_expert=w2,
+    )
+
+
+def flops(wl, routes):
+    return 6.0 * wl.H * wl.I * routes
+
+
+# ------------------------------------------------------------------ cpu baseline
+def cpu_baseline(wl, min_seconds=10.0):
+    """The oracle as it stands, on the host cores, over every token of the
+    workload (repeated until ~min_seconds of CPU work)."""
+    import oracle
+    import synth
+    p = oracle.quantize_problem(synth.make_raw(wl))
+    toks = np.arange(wl.M, dtype=np.int32)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward_tokens(p, toks)
+        n += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=wl.M * n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"all {wl.M} tokens of {wl.name}, {n} pass(es) in {dt:.1f} s (fp64 C oracle, OpenMP)")
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=6, help="resident input copies rotated over steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--workload", default="w4a16_decode")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the expert-parallel sharding across GPUs is a design, "
+              "not code); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    import synth
+    moe.lib()  # fail loudly if the native library is missing
+    assert torch.cuda.is_available(), "no GPU"
+    wl = synth.WORKLOADS[args.workload]
+
+    log(f"bench: {wl.name}: {args.steps} steps after {args.warmup} warm-up")
+    r = time_workload(wl, args.steps, args.warmup, args.copies)
+    routes, active = r["local_routes"], r["active_experts"]
+    by = w4a16_bytes(wl, routes, active)
+    fl = flops(wl, routes)
+    sec = r["seconds"]
+    tokens_s = wl.M * args.steps / sec
+    g1_ms = r["phase_ms"]["gemm1"]
+    g1_gbs = by["gemm1"] / (g1_ms * 1e-3) / 1e9
+    fwd_gbs = by["weights"] / (r["ms_per_step"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "quant_mode": "w4a16 (NVFP4 weights, bf16 activations)", "M": wl.M,
+                   "H": wl.H, "I": wl.I, "num_experts": wl.num_experts, "num_local_experts": wl.num_local_experts,
+                   "top_k": wl.top_k, "tile": r["tile"], "finalize": "deterministic", "local_routes": routes,
+                   "active_local_experts": active, "resident_copies": args.copies},
+        "roofline": {"bound": "hbm", "kernel": "grouped_gemm1_swiglu", "achieved": g1_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": g1_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": by["gemm1"], "avg_ms": g1_ms},
+        "forward": {"weight_bytes": by["weights"], "weight_GBps": fwd_gbs, "hbm_frac": fwd_gbs / HBM_PEAK_GBS,
+                    "tflops": fl / (r["ms_per_step"] * 1e-3) / 1e12, "phase_ms": r["phase_ms"],
+                    "ms_per_step_with_events": r["ms_per_step_with_events"]},
+    }
+    if not args.no_secondary:
+        wl2 = synth.WORKLOADS["w4a16_prefill"]
+        steps2 = max(10, args.steps // 4)
+        log(f"bench: {wl2.name}: {steps2} steps")
+        r2 = time_workload(wl2, steps2, max(3, args.warmup // 4), args.copies)
+        fl2 = flops(wl2, r2["local_routes"])
+        tf2 = fl2 / (r2["ms_per_step"] * 1e-3) / 1e12
+        g1f = 4.0 * wl2.H * wl2.I * r2["local_routes"] / (r2["phase_ms"]["gemm1"] * 1e-3) / 1e12
+        line["prefill"] = {"workload": wl2.name, "M": wl2.M, "tokens_per_s": wl2.M * steps2 / r2["seconds"],
+                           "ms_per_step": r2["ms_per_step"], "tile": r2["tile"], "local_routes": r2["local_routes"],
+                           "tflops": tf2, "mfma_frac": tf2 / BF16_PEAK_TFLOPS, "gemm1_tflops": g1f,
+                           "gemm1_mfma_frac": g1f / BF16_PEAK_TFLOPS, "phase_ms": r2["phase_ms"],
+                           "peak_tflops": BF16_PEAK_TFLOPS}
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -210,7 +210,8 @@ typedef struct moe_opts {
   int route_order;               /* moe_route_order_t, default AUTO */
   int tile;                      /* route tile; 0 = moe_default_tile() */
   int64_t x_row_stride;          /* 0 = contiguous rows */
-  void* workspace;               /* device, >= moe_workspace_size() bytes, 256-byte aligned */
+  void* workspace;               /* device, >= moe_workspace_size() bytes, 256-byte aligned,
+                                    zero-filled before its first moe_forward (see below) */
   size_t workspace_bytes;
   void** phase_events;           /* optional: MOE_NUM_PHASE_EVENTS hipEvent_t recorded on the
                                     stream before sort, after sort, after GEMM1, after GEMM2,
@@ -224,8 +225,15 @@ void moe_opts_init(moe_opts_t* opts);
 /* The route tile moe_forward uses when opts->tile == 0. */
 int moe_default_tile(int M, int top_k, int num_local_experts, moe_quant_mode_t mode);
 
-/* Device workspace of moe_forward: the plan, y1 (+ y1_sf) and, in
- * deterministic mode, y2. */
+/* Device workspace of moe_forward: a block of MOE_WORKSPACE_COUNTER_BYTES
+ * of counters, the plan, y1 (+ y1_sf) and, in deterministic mode or on the
+ * decode path, y2.  The counter block must be zero before the first
+ * moe_forward that uses the workspace (zero-fill the allocation, or its
+ * first MOE_WORKSPACE_COUNTER_BYTES, once); every call leaves it zero
+ * again, and no other entry point writes it.  The counters coordinate the
+ * workgroups of the decode path's single launch, so two moe_forward calls
+ * in flight at once must not share a workspace. */
+#define MOE_WORKSPACE_COUNTER_BYTES 401664
 size_t moe_workspace_size(int M, int H, int I, int top_k, int num_local_experts, int tile,
                           moe_quant_mode_t mode, int finalize_mode);
 
@@ -237,8 +245,11 @@ size_t moe_workspace_size(int M, int H, int I, int top_k, int num_local_experts,
  *   out: bf16 [M, H], overwritten (accumulate = 0) or added to.
  * Enqueues moe_sort, moe_grouped_gemm1_swiglu, moe_grouped_gemm2 and (in
  * deterministic mode) moe_finalize; in atomic mode with accumulate = 0 the
- * output is zero-filled first by a kernel.  `out` is this GPU's share: the
- * sum over its local routes only. */
+ * output is zero-filled first by a kernel.  Decode-sized W4A16 batches
+ * (tile 16, M * top_k <= 1024, H a multiple of 1024 and at most 65536,
+ * I a multiple of 512) take a single persistent launch instead that does
+ * all four steps; its finalize is the deterministic one in either mode.
+ * `out` is this GPU's share: the sum over its local routes only. */
 moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk_ids, const float* topk_weights,
                          const uint8_t* w1, const uint8_t* w1_sf, const float* w1_alpha, const uint8_t* w2,
                          const uint8_t* w2_sf, const float* w2_alpha, int num_experts, int top_k,

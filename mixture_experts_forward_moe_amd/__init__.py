@@ -17,6 +17,7 @@ W4A16, W4A4, MXFP8_MXFP4 = 0, 1, 2
 FINALIZE_DETERMINISTIC, FINALIZE_ATOMIC = 0, 1
 ROUTE_ORDER_AUTO, ROUTE_ORDER_SINGLE, ROUTE_ORDER_SPAN = 0, 1, 2
 NUM_PHASE_EVENTS = 5
+WORKSPACE_COUNTER_BYTES = 401664  # the forward workspace's counter block (MOE_WORKSPACE_COUNTER_BYTES)
 FLT_MAX = 3.4028234663852886e38
 
 EXPORTS = [
@@ -125,8 +126,9 @@ def workspace_size(M, H, I, top_k, num_local_experts, tile, mode, finalize_mode=
 
 def _alloc(nbytes: int, device):
     import torch
-    # 256-byte alignment: torch's caching allocator aligns blocks to 512 bytes
-    t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    # 256-byte alignment: torch's caching allocator aligns blocks to 512 bytes.
+    # Zero-filled: a forward workspace's counter block starts at zero.
+    t = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
     assert t.data_ptr() % 256 == 0
     return t
 

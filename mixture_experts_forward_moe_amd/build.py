@@ -9,13 +9,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["sort.hip", "gemm.hip", "finalize.hip", "capi.cpp"]
+SOURCES = ["sort.hip", "gemm.hip", "stream.hip", "decode.hip", "finalize.hip", "capi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
     # keep packed fp32 instructions out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# per-source extras: the decode kernel's thread-0 counter claims must stay
+# plain atomics (a wavefront-aggregated rewrite waits for the result at once)
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -26,7 +29,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-        cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
     failed = []
     for src, p in procs:

@@ -250,16 +250,32 @@ int moe_default_tile(int M, int top_k, int num_local_experts, moe_quant_mode_t m
   return 64;
 }
 
+static_assert(MOE_WORKSPACE_COUNTER_BYTES == DEC_COUNTER_BYTES, "counter block size in moe.h");
+
 size_t moe_workspace_size(int M, int H, int I, int top_k, int num_local_experts, int tile, moe_quant_mode_t mode,
                           int finalize_mode) {
   if (!plan_args_ok(M, top_k, num_local_experts, tile) || !mode_ok(mode) || H <= 0 || I <= 0) return 0;
   PlanLayout L = plan_layout(M, top_k, num_local_experts, tile);
-  size_t total = L.total;
+  // the decode path's counter block first, at a place no shape moves
+  size_t total = DEC_COUNTER_BYTES + L.total;
   total = align256(total + y1_bytes(mode, L.slots, I));
   total = align256(total + y1_sf_bytes(mode, L.slots, I));
-  if (finalize_mode == MOE_FINALIZE_DETERMINISTIC) total = align256(total + (size_t)L.slots * H * 2);
+  const bool dec = tile == 16 && decode_supported(mode, M, top_k, num_local_experts, H, I);
+  if (finalize_mode == MOE_FINALIZE_DETERMINISTIC || dec) total = align256(total + (size_t)L.slots * H * 2);
   return total;
 }
+
+namespace {
+struct MarkCtx {
+  hipEvent_t* ev;
+  hipStream_t st;
+  hipError_t err;
+};
+void mark_phase(void* ctx, int i) {
+  MarkCtx* c = (MarkCtx*)ctx;
+  if (c->ev && c->ev[i] && c->err == hipSuccess) c->err = hipEventRecord(c->ev[i], c->st);
+}
+}  // namespace
 
 moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk_ids, const float* topk_weights,
                          const uint8_t* w1, const uint8_t* w1_sf, const float* w1_alpha, const uint8_t* w2,
@@ -287,14 +303,18 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
 
   moe_plan_t plan;
   PlanLayout L = plan_layout(M, top_k, num_local_experts, tile);
-  s = moe_plan_init(&plan, opts->workspace, L.total, M, top_k, num_local_experts, tile);
+  int* counters = (int*)opts->workspace;
+  uint8_t* base = (uint8_t*)opts->workspace + DEC_COUNTER_BYTES;
+  s = moe_plan_init(&plan, base, L.total, M, top_k, num_local_experts, tile);
   if (s != MOE_OK) return s;
-  uint8_t* base = (uint8_t*)opts->workspace + L.total;
+  base += L.total;
   void* y1 = base;
   base += align256(y1_bytes(quant_mode, L.slots, I));
   uint8_t* y1_sf = (quant_mode == MOE_QUANT_W4A16) ? NULL : base;
   base += align256(y1_sf_bytes(quant_mode, L.slots, I));
-  uint16_t* y2 = (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC) ? (uint16_t*)base : NULL;
+  const bool dec = tile == 16 && decode_supported(quant_mode, M, top_k, num_local_experts, H, I) &&
+                   opts->x_row_stride % 8 == 0;
+  uint16_t* y2 = (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC || dec) ? (uint16_t*)base : NULL;
 
   hipStream_t st = (hipStream_t)stream;
   hipEvent_t* ev = (hipEvent_t*)opts->phase_events;
@@ -306,11 +326,47 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
       if (mark(i) != hipSuccess) return MOE_ERR_DEVICE;
     return MOE_OK;
   }
+  if (dec) {
+    // decode-sized batch: plan, GEMM1, GEMM2 and finalize in one launch
+    DecodeParams d;
+    d.topk_ids = topk_ids;
+    d.local_expert_offset = local_expert_offset;
+    d.x = x;
+    d.x_row_stride = opts->x_row_stride ? opts->x_row_stride : H;
+    d.w1 = w1;
+    d.w1_sf = w1_sf;
+    d.w1_alpha = w1_alpha;
+    d.w2 = w2;
+    d.w2_sf = w2_sf;
+    d.w2_alpha = w2_alpha;
+    d.H = H;
+    d.I = I;
+    d.swiglu_alpha = opts->swiglu_alpha;
+    d.swiglu_beta = opts->swiglu_beta;
+    d.swiglu_limit = opts->swiglu_limit;
+    d.y1 = (uint16_t*)y1;
+    d.y2 = y2;
+    d.counters = counters;
+    d.topk_weights = topk_weights;
+    d.routed_scaling_factor = opts->routed_scaling_factor;
+    d.accumulate = opts->accumulate;
+    d.out = out;
+    d.plan = &plan;
+    MarkCtx mc = {ev, st, hipSuccess};
+    d.mark = mark_phase;
+    d.mark_ctx = &mc;
+    if (launch_decode(d, st) != hipSuccess || mc.err != hipSuccess) return MOE_ERR_DEVICE;
+    if (mark(4) != hipSuccess) return MOE_ERR_DEVICE;
+    return MOE_OK;
+  }
   s = moe_sort(topk_ids, M, top_k, num_experts, num_local_experts, local_expert_offset,
                (moe_route_order_t)opts->route_order, &plan, stream);
   if (s != MOE_OK) return s;
   if (mark(1) != hipSuccess) return MOE_ERR_DEVICE;
-  if (opts->finalize_mode == MOE_FINALIZE_ATOMIC && !opts->accumulate) {
+  // small tiles: GEMM2 streams the weights and finalizes in route order in
+  // the same kernel (deterministic in either finalize mode)
+  const bool fused = stream_supported(quant_mode, &plan, H, I);
+  if (!fused && opts->finalize_mode == MOE_FINALIZE_ATOMIC && !opts->accumulate) {
     if (launch_zero_fill(out, (size_t)M * H * 2, st) != hipSuccess) return MOE_ERR_DEVICE;
   }
   s = moe_grouped_gemm1_swiglu(quant_mode, x, x_sf, opts->x_row_stride, &plan, w1, w1_sf, w1_alpha, H, I,
@@ -318,7 +374,24 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
                                y1_sf, stream);
   if (s != MOE_OK) return s;
   if (mark(2) != hipSuccess) return MOE_ERR_DEVICE;
-  if (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC) {
+  if (fused) {
+    Gemm2Params p;
+    p.mode = quant_mode;
+    p.y1 = y1;
+    p.y1_sf = y1_sf;
+    p.plan = &plan;
+    p.w2 = w2;
+    p.w2_sf = w2_sf;
+    p.w2_alpha = w2_alpha;
+    p.H = H;
+    p.I = I;
+    p.y2 = NULL;
+    p.topk_weights = topk_weights;
+    p.routed_scaling_factor = opts->routed_scaling_factor;
+    p.out = out;
+    if (launch_gemm2_stream(p, opts->accumulate, st) != hipSuccess) return MOE_ERR_DEVICE;
+    if (mark(3) != hipSuccess) return MOE_ERR_DEVICE;
+  } else if (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC) {
     s = moe_grouped_gemm2(quant_mode, y1, y1_sf, &plan, w2, w2_sf, w2_alpha, H, I, y2, NULL,
                           opts->routed_scaling_factor, NULL, stream);
     if (s != MOE_OK) return s;

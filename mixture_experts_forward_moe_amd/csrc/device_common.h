@@ -121,11 +121,12 @@ DEV float warp_max16(float v) {
 }
 
 // SwiGLU with alpha / beta / limit on fp32 gate and up values:
-// min(g, l) * sigmoid(a * min(g, l)) * (clamp(u, -l, l) + b)
+// min(g, l) * sigmoid(a * min(g, l)) * (clamp(u, -l, l) + b).  The sigmoid
+// uses the accurate expf and a correctly rounded divide, so y lands within
+// about one fp32 ulp of the exact value before its single bf16 rounding.
 DEV float swiglu_f32(float g, float u, float alpha, float beta, float limit) {
   float gc = fminf(g, limit);
   float uc = fminf(fmaxf(u, -limit), limit);
-  float e = __expf(-alpha * gc);
-  float sig = __frcp_rn(1.0f + e);
+  float sig = 1.0f / (1.0f + expf(-alpha * gc));
   return gc * sig * (uc + beta);
 }

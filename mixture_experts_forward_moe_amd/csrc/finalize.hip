@@ -11,6 +11,10 @@
 #include "device_common.h"
 #include "internal.h"
 
+// The finalize's multiplies and adds are separate roundings (no fused
+// multiply-add), as the route-order reduction states them.
+#pragma clang fp contract(off)
+
 namespace moe {
 
 constexpr int FIN_THREADS = 256;
@@ -37,11 +41,11 @@ __global__ __launch_bounds__(FIN_THREADS) void finalize_kernel(const uint16_t* _
   for (int j = 0; j < top_k; j++) {
     const int32_t s = e2p[t * top_k + j];
     if (s < 0) continue;
-    const float wf = __fmul_rn(w[t * top_k + j], rsf);
+    const float wf = w[t * top_k + j] * rsf;
     u32x4_t v = *reinterpret_cast<const u32x4_t*>(y2 + (int64_t)s * H + h0);
     for (int i = 0; i < 4; i++) {
-      acc[2 * i] = __fadd_rn(acc[2 * i], __fmul_rn(wf, __uint_as_float(v[i] << 16)));
-      acc[2 * i + 1] = __fadd_rn(acc[2 * i + 1], __fmul_rn(wf, __uint_as_float(v[i] & 0xffff0000u)));
+      acc[2 * i] = acc[2 * i] + wf * __uint_as_float(v[i] << 16);
+      acc[2 * i + 1] = acc[2 * i + 1] + wf * __uint_as_float(v[i] & 0xffff0000u);
     }
   }
   u32x4_t r;

@@ -459,6 +459,7 @@ static void plan_args(KArgs& a, const moe_plan_t* plan, int bm) {
 }
 
 hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
+  if (stream_supported(p.mode, p.plan, p.H, p.I)) return launch_gemm1_stream(p, stream);
   KArgs a = {};
   const int bm = pick_bm(p.plan->tile);
   plan_args(a, p.plan, bm);
@@ -486,6 +487,7 @@ hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
 }
 
 hipError_t launch_gemm2(const Gemm2Params& p, hipStream_t stream) {
+  if (!p.out && stream_supported(p.mode, p.plan, p.H, p.I)) return launch_gemm2_stream(p, 0, stream);
   KArgs a = {};
   const int bm = pick_bm(p.plan->tile);
   plan_args(a, p.plan, bm);

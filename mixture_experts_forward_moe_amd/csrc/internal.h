@@ -49,6 +49,47 @@ struct Gemm2Params {
 hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream);
 hipError_t launch_gemm2(const Gemm2Params& p, hipStream_t stream);
 
+// weight-streaming kernels for 16-slot tiles (decode-sized batches)
+bool stream_supported(int mode, const moe_plan_t* plan, int H, int I);
+hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream);
+// y2 rows (p.y2) or, with p.out, the fused deterministic finalize into out
+hipError_t launch_gemm2_stream(const Gemm2Params& p, int accumulate, hipStream_t stream);
+
+// the two-launch W4A16 forward for decode-sized batches (plan tile 16)
+struct DecodeParams {
+  const int32_t* topk_ids;
+  int local_expert_offset;
+  const void* x;
+  int64_t x_row_stride;  // elements
+  const uint8_t *w1, *w1_sf;
+  const float* w1_alpha;
+  const uint8_t *w2, *w2_sf;
+  const float* w2_alpha;
+  int H, I;
+  float swiglu_alpha, swiglu_beta, swiglu_limit;
+  uint16_t* y1;
+  uint16_t* y2;
+  int* counters;  // the decode counter block (DEC_COUNTER_BYTES), zero between calls
+  const float* topk_weights;
+  float routed_scaling_factor;
+  int accumulate;
+  uint16_t* out;
+  const moe_plan_t* plan;
+  void (*mark)(void* ctx, int phase);  // optional: called between the launches
+  void* mark_ctx;
+};
+// Decode path limits.  Its counter block sits at the head of the forward
+// workspace: a head slot (finalized column groups, stalled waits), one
+// ready count per plan tile and one done count per 64 columns of H, each
+// in a 256-byte slot of its own.
+constexpr int DEC_MAX_ROUTES = 1024;
+constexpr int DEC_MAX_TILES = (DEC_MAX_ROUTES + MAX_LOCAL_EXPERTS * 15) / 16;  // 16-slot tiles
+constexpr int DEC_MAX_COL_GROUPS = 1024;                                       // H <= 65536
+constexpr int DEC_CTR_SLOT = 64;                                               // ints per counter slot
+constexpr size_t DEC_COUNTER_BYTES = sizeof(int) * DEC_CTR_SLOT * (1 + DEC_MAX_TILES + DEC_MAX_COL_GROUPS);
+bool decode_supported(int mode, int M, int top_k, int El, int H, int I);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
 // finalize and fills
 hipError_t launch_finalize(const uint16_t* y2, const int32_t* e2p, const float* w, int64_t M, int top_k, int H,
                            float rsf, int accumulate, uint16_t* out, hipStream_t stream);

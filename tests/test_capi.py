@@ -122,3 +122,14 @@ def test_workspace_size_grows_with_mode():
     c = moe.workspace_size(16, 256, 512, 2, 8, 16, 1, 0)   # NVFP4 y1 is smaller than bf16
     assert a > b > 0 and a > c > 0
     assert moe.default_tile(8, 8, 32, 0) == 16
+
+
+def test_header_constants_match_binding():
+    """The constants moe.h defines are the binding's."""
+    import re
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define\s+(MOE_\w+)\s+(\d+)", text))
+    assert int(consts["MOE_WORKSPACE_COUNTER_BYTES"]) == moe.WORKSPACE_COUNTER_BYTES
+    assert int(consts["MOE_NUM_PHASE_EVENTS"]) == moe.NUM_PHASE_EVENTS
+    # the counter block leads every forward workspace
+    assert moe.workspace_size(8, 1024, 512, 8, 32, 16, 0) > moe.WORKSPACE_COUNTER_BYTES

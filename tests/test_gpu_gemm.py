@@ -16,6 +16,9 @@ CASES = {
     "w4a16_offset_swiglu": (oracle.W4A16, dict(M=37, H=384, I=256, E=16, El=6, k=4, seed=42, offset=5,
                                                swiglu_limit=0.3, swiglu_alpha=1.702, swiglu_beta=1.0)),
     "w4a16_wide": (oracle.W4A16, dict(M=70, H=512, I=384, E=4, El=4, k=3, seed=43)),
+    "w4a16_stream": (oracle.W4A16, dict(M=60, H=512, I=512, E=8, El=8, k=3, seed=48)),
+    "w4a16_stream_offset": (oracle.W4A16, dict(M=23, H=1024, I=512, E=64, El=16, k=6, seed=49, offset=16,
+                                               swiglu_limit=0.5)),
     "w4a4_basic": (oracle.W4A4, dict(M=40, H=256, I=256, E=8, El=8, k=2, seed=44)),
     "w4a4_offset": (oracle.W4A4, dict(M=33, H=384, I=128, E=12, El=5, k=3, seed=45, offset=7)),
     "mx_basic": (oracle.MXFP8_MXFP4, dict(M=40, H=256, I=256, E=8, El=8, k=2, seed=46)),
@@ -105,7 +108,7 @@ def test_forward(name, tile):
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("name", ["w4a16_basic", "w4a4_offset", "mx_offset"])
+@pytest.mark.parametrize("name", ["w4a16_basic", "w4a16_stream_offset", "w4a4_offset", "mx_offset"])
 def test_atomic_finalize_and_accumulate(name):
     import torch
 
@@ -144,3 +147,87 @@ def test_row_strided_x():
     out = d.forward(x_row_stride=p.H + 64)
     torch.cuda.synchronize()
     check_close(host(out, np.uint16), oracle.forward_tokens(p, np.arange(p.M)), p.mode, "strided")
+
+
+def takes_decode_path(p, tile=16):
+    """The single-launch decode path keeps y2 in its workspace in either
+    finalize mode; the tiled path keeps it in deterministic mode only."""
+    import mixture_experts_forward_moe_amd as moe
+    args = (p.M, p.H, p.I, p.top_k, p.num_local_experts, tile, p.mode)
+    return moe.workspace_size(*args, moe.FINALIZE_ATOMIC) == moe.workspace_size(*args, moe.FINALIZE_DETERMINISTIC)
+
+
+def decode_case(case):
+    if case == "no_local_routes":
+        wl = synth.small_workload(oracle.W4A16, 6, 1024, 512, 64, 8, 4, 51, offset=8)
+        raw = synth.make_raw(wl)
+        raw.topk_ids[:] = np.where(raw.topk_ids < 16, raw.topk_ids + 16, raw.topk_ids)
+    elif case == "hot_experts":
+        # 40 routes per expert: three tiles each, the last one ragged
+        wl = synth.small_workload(oracle.W4A16, 40, 1024, 1024, 2, 2, 2, 52)
+        raw = synth.make_raw(wl)
+    elif case == "one_token":
+        wl = synth.small_workload(oracle.W4A16, 1, 1024, 512, 16, 16, 4, 53)
+        raw = synth.make_raw(wl)
+    else:  # "offset_swiglu": a local window of the experts, clamped SwiGLU
+        wl = synth.small_workload(oracle.W4A16, 9, 2048, 1536, 64, 16, 6, 54, offset=24, swiglu_limit=0.4,
+                                  swiglu_alpha=1.702, swiglu_beta=1.0)
+        raw = synth.make_raw(wl)
+    return oracle.quantize_problem(raw)
+
+
+@pytest.mark.parametrize("case", ["no_local_routes", "hot_experts", "one_token", "offset_swiglu"])
+def test_decode_path_edge_cases(case):
+    """Decode-sized batches (tile 16) through the single-launch path: no
+    local route at all, experts with several tiles and a ragged last tile,
+    a single token, an expert window with a clamped SwiGLU."""
+    import torch
+
+    from gpu_util import DeviceProblem, check_close, dev, host, say
+    say(f"decode edge case {case}")
+    p = decode_case(case)
+    assert takes_decode_path(p)
+    d = DeviceProblem(p)
+    out = d.forward(tile=16)
+    torch.cuda.synchronize()
+    want = oracle.forward_tokens(p, np.arange(p.M))
+    if case == "no_local_routes":
+        assert np.all(host(out, np.uint16) == 0) and np.all(want == 0)
+        prev = synth.normal_bf16(3, 3, (p.M, p.H))
+        out = dev(prev.copy())
+        d.forward(out=out, tile=16, accumulate=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out, np.uint16), prev)
+    else:
+        check_close(host(out, np.uint16), want, p.mode, f"decode {case}")
+        prev = synth.normal_bf16(8, 8, (p.M, p.H), 0.0, 0.01)
+        acc = dev(prev.copy())
+        d.forward(out=acc, tile=16, accumulate=True)
+        torch.cuda.synchronize()
+        check_close(host(acc, np.uint16), oracle.forward_tokens(p, np.arange(p.M), accumulate=True, out_prev=prev),
+                    p.mode, f"decode {case} accumulate")
+
+
+def test_decode_path_workspace_reuse():
+    """One workspace through many calls: the decode launch's counters must
+    come back to zero after every call, whatever shape came before (a
+    tiled-path call in between included), and results stay bit-identical."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, host, say
+    say("decode workspace reuse")
+    probs = [decode_case("offset_swiglu"), decode_case("hot_experts"), decode_case("one_token"),
+             problem("w4a16_basic")]
+    sizes = [moe.workspace_size(p.M, p.H, p.I, p.top_k, p.num_local_experts, 16, p.mode) for p in probs]
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device="cuda")
+    devs = [DeviceProblem(p) for p in probs]
+    first = [d.forward(tile=16) for d in devs]  # fresh workspace each
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i in [0, 1, 3, 2, 0, 2, 1]:
+            out = devs[i].forward(tile=16, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out, first[i]), (rep, i)
+    counters = host(ws[:moe.WORKSPACE_COUNTER_BYTES].view(torch.int32))
+    assert np.all(counters == 0), np.nonzero(counters)
