@@ -87,10 +87,62 @@ class GpuInputs:
         return routes, active
 
 
-def time_workload(wl, steps: int, warmup: int, copies: int):
-    """Times `steps` forwards twice on the same resident inputs: once bare
-    (the headline), once with HIP events recorded by moe_forward between its
-    launches on the same stream (per-kernel durations)."""
+def _opts(moe, wl, ws, tile, **kw):
+    return moe.make_opts(workspace=ws, tile=tile, swiglu_alpha=wl.swiglu_alpha, swiglu_beta=wl.swiglu_beta,
+                         swiglu_limit=wl.swiglu_limit, **kw)
+
+
+def time_graph(wl, steps: int, warmup: int, copies: int):
+    """Times `steps` forwards replayed from a HIP graph that holds `copies`
+    forwards, one per resident input copy (no host work between launches).
+    HIP events on the replay stream bracket the timed replays."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    g = GpuInputs(wl, copies)
+    H, I, E = wl.H, wl.I, wl.num_local_experts
+    tile = moe.default_tile(wl.M, wl.top_k, E, wl.mode)
+    ws = torch.zeros(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.M, H), dtype=torch.int16, device="cuda")
+    opts = _opts(moe, wl, ws, tile)
+
+    def step(i):
+        x, ids, w, w1, w1s, w1a, w2, w2s, w2a = g.copies[i % len(g.copies)]
+        moe.moe_forward(x, None, ids, w, w1, w1s, w1a, w2, w2s, w2a, wl.num_experts, wl.top_k, E,
+                        wl.local_expert_offset, wl.mode, out, H, I, opts=opts)
+
+    for i in range(max(warmup, copies)):  # eager warm-up (also caches the launch shape)
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(copies):
+            step(i)
+    reps = max(1, steps // copies)
+    for _ in range(max(1, warmup // copies)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    n = reps * copies
+    gpu_ms = e0.elapsed_time(e1)
+    routes, active = g.local_stats()
+    del graph, g
+    torch.cuda.empty_cache()
+    return dict(steps=n, seconds=dt, ms_per_step=dt * 1e3 / n, gpu_ms_per_step=gpu_ms / n, tile=tile,
+                local_routes=routes, active_experts=active)
+
+
+def time_phases(wl, steps: int, warmup: int, copies: int):
+    """Times `steps` eager forwards, then the same steps again with HIP
+    events that moe_forward records between its launches on the same
+    stream (per-kernel durations)."""
     import torch
 
     import mixture_experts_forward_moe_amd as moe
@@ -105,10 +157,8 @@ def time_workload(wl, steps: int, warmup: int, copies: int):
         for e in row:
             e.record()
     torch.cuda.synchronize()
-    opts = [moe.make_opts(workspace=ws, tile=tile, swiglu_alpha=wl.swiglu_alpha, swiglu_beta=wl.swiglu_beta,
-                          swiglu_limit=wl.swiglu_limit)]
-    opts_ev = [moe.make_opts(workspace=ws, tile=tile, swiglu_alpha=wl.swiglu_alpha, swiglu_beta=wl.swiglu_beta,
-                             swiglu_limit=wl.swiglu_limit, phase_events=events[i]) for i in range(steps)]
+    opts = _opts(moe, wl, ws, tile)
+    opts_ev = [_opts(moe, wl, ws, tile, phase_events=events[i]) for i in range(steps)]
 
     def step(i, o):
         x, ids, w, w1, w1s, w1a, w2, w2s, w2a = g.copies[i % len(g.copies)]
@@ -116,43 +166,41 @@ def time_workload(wl, steps: int, warmup: int, copies: int):
                         wl.local_expert_offset, wl.mode, out, H, I, opts=o)
 
     for i in range(warmup):
-        step(i, opts[0])
+        step(i, opts)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, opts[0])
+        step(i, opts)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    # the same steps with per-phase events
-    t1 = time.perf_counter()
     for i in range(steps):
         step(i, opts_ev[i])
     torch.cuda.synchronize()
-    dt_ev = time.perf_counter() - t1
     names = ["sort", "gemm1", "gemm2", "finalize"]
     per = {n: float(np.mean([events[i][k].elapsed_time(events[i][k + 1]) for i in range(steps)]))
            for k, n in enumerate(names)}
-    res = dict(seconds=dt, ms_per_step=dt * 1e3 / steps, ms_per_step_with_events=dt_ev * 1e3 / steps, tile=tile,
-               phase_ms=per)
     routes, active = g.local_stats()
-    res["local_routes"] = routes
-    res["active_experts"] = active
     del g
     torch.cuda.empty_cache()
-    return res
+    return dict(steps=steps, seconds=dt, ms_per_step=dt * 1e3 / steps, tile=tile, phase_ms=per,
+                local_routes=routes, active_experts=active)
 
 
 # ------------------------------------------------------------------ algorithmic work
 def w4a16_bytes(wl, routes, active):
     """Algorithmic HBM bytes: active experts' NVFP4 weights (codes + E4M3
-    block scales), each token's bf16 row read once, y1/y2 written and read
-    once per local route, the output written once."""
+    block scales); per local route its token's bf16 row read, y1 written and
+    read, y2 written and read; routing ids and weights read; the output
+    written once."""
     H, I = wl.H, wl.I
     w1 = 2 * I * H // 2 + 2 * I * H // 16
     w2 = H * I // 2 + H * I // 16
+    act = routes * (2 * H + 2 * 2 * I + 2 * 2 * H)
+    io = wl.M * wl.top_k * 8 + wl.M * H * 2
     return dict(
         gemm1=active * w1 + routes * (H * 2 + I * 2),
         gemm2=active * w2 + routes * (I * 2 + H * 2),
+        forward=active * (w1 + w2) + act + io,
         weights=active * (w1 + w2),
         w1_per_expert=w1, w2_per_expert=w2,
     )
@@ -160,6 +208,23 @@ def w4a16_bytes(wl, routes, active):
 
 def flops(wl, routes):
     return 6.0 * wl.H * wl.I * routes
+
+
+# ------------------------------------------------------------------ measured traffic
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record of this kernel and workload, scaled by the copy
+    calibration; None when there is no record or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 # ------------------------------------------------------------------ cpu baseline
@@ -182,6 +247,28 @@ def cpu_baseline(wl, min_seconds=10.0):
                 sample=f"all {wl.M} tokens of {wl.name}, {n} pass(es) in {dt:.1f} s (fp64 C oracle, OpenMP)")
 
 
+# ------------------------------------------------------------------ counter calibration
+def copy_calibration(steps: int, nbytes: int = 1 << 28):
+    """A plain device-to-device copy of nbytes, `steps` times: its
+    FETCH_SIZE / WRITE_SIZE per dispatch against nbytes gives the factor
+    that turns those counters into HBM bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes": nbytes, "read_bytes": nbytes, "write_bytes": nbytes, "steps": steps,
+                      "ms_per_copy": ms, "GBps_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -192,6 +279,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--workload", default="w4a16_decode")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the expert-parallel sharding across GPUs is a design, "
@@ -200,28 +289,32 @@ def main():
 
     import torch
 
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     import mixture_experts_forward_moe_amd as moe
     import synth
     moe.lib()  # fail loudly if the native library is missing
     assert torch.cuda.is_available(), "no GPU"
     wl = synth.WORKLOADS[args.workload]
 
-    log(f"bench: {wl.name}: {args.steps} steps after {args.warmup} warm-up")
-    r = time_workload(wl, args.steps, args.warmup, args.copies)
+    log(f"bench: {wl.name}: {args.steps} steps after {args.warmup} warm-up (graph replay)")
+    r = time_graph(wl, args.steps, args.warmup, args.copies)
     routes, active = r["local_routes"], r["active_experts"]
     by = w4a16_bytes(wl, routes, active)
     fl = flops(wl, routes)
-    sec = r["seconds"]
-    tokens_s = wl.M * args.steps / sec
-    g1_ms = r["phase_ms"]["gemm1"]
-    g1_gbs = by["gemm1"] / (g1_ms * 1e-3) / 1e9
-    fwd_gbs = by["weights"] / (r["ms_per_step"] * 1e-3) / 1e9
+    tokens_s = wl.M * r["steps"] / r["seconds"]
+    # the decode forward is one kernel (dec_fused_kernel): its per-launch
+    # time is the replay time per step, measured with events on the stream
+    k_ms = r["gpu_ms_per_step"]
+    k_gbs = by["forward"] / (k_ms * 1e-3) / 1e9
+    w_gbs = by["weights"] / (k_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": tokens_s,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": r["steps"],
         "warmup": args.warmup,
         "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
@@ -232,19 +325,19 @@ def main():
         "config": {"workload": wl.name, "quant_mode": "w4a16 (NVFP4 weights, bf16 activations)", "M": wl.M,
                    "H": wl.H, "I": wl.I, "num_experts": wl.num_experts, "num_local_experts": wl.num_local_experts,
                    "top_k": wl.top_k, "tile": r["tile"], "finalize": "deterministic", "local_routes": routes,
-                   "active_local_experts": active, "resident_copies": args.copies},
-        "roofline": {"bound": "hbm", "kernel": "grouped_gemm1_swiglu", "achieved": g1_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": g1_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes": by["gemm1"], "avg_ms": g1_ms},
-        "forward": {"weight_bytes": by["weights"], "weight_GBps": fwd_gbs, "hbm_frac": fwd_gbs / HBM_PEAK_GBS,
-                    "tflops": fl / (r["ms_per_step"] * 1e-3) / 1e12, "phase_ms": r["phase_ms"],
-                    "ms_per_step_with_events": r["ms_per_step_with_events"]},
+                   "active_local_experts": active, "resident_copies": args.copies, "launch": "hip graph replay"},
+        "roofline": {"bound": "hbm", "kernel": "dec_fused_kernel", "achieved": k_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": k_gbs / HBM_PEAK_GBS,
+                     "traffic": counter_traffic("dec_fused_kernel", wl.name),
+                     "algorithmic_bytes": by["forward"], "avg_ms": k_ms},
+        "weights": {"bytes": by["weights"], "GBps": w_gbs, "hbm_frac": w_gbs / HBM_PEAK_GBS,
+                    "tflops": fl / (k_ms * 1e-3) / 1e12},
     }
     if not args.no_secondary:
         wl2 = synth.WORKLOADS["w4a16_prefill"]
-        steps2 = max(10, args.steps // 4)
-        log(f"bench: {wl2.name}: {steps2} steps")
-        r2 = time_workload(wl2, steps2, max(3, args.warmup // 4), args.copies)
+        steps2 = max(10, args.steps // 10)
+        log(f"bench: {wl2.name}: {steps2} steps (eager, per-kernel events)")
+        r2 = time_phases(wl2, steps2, max(3, args.warmup // 4), args.copies)
         fl2 = flops(wl2, r2["local_routes"])
         tf2 = fl2 / (r2["ms_per_step"] * 1e-3) / 1e12
         g1f = 4.0 * wl2.H * wl2.I * r2["local_routes"] / (r2["phase_ms"]["gemm1"] * 1e-3) / 1e12

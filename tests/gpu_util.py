@@ -61,9 +61,12 @@ def bf16(bits):
     return synth.bf16_to_f32(np.asarray(bits).view(np.uint16)).astype(np.float64)
 
 
-def check_close(got_bits, ref_bits, mode, what=""):
+def check_close(got_bits, ref_bits, mode, what="", max_bar=True):
     """The parity bar: rel-L2 <= 5e-3 and |err| <= 1e-2 max|ref| (W4A16, MX);
-    rel-L2 <= 2e-2 (W4A4 with its NVFP4 requantisation)."""
+    rel-L2 <= 2e-2 (W4A4 with its NVFP4 requantisation).  max_bar=False
+    leaves out the max-error part: for a requantising pass compared end to
+    end, where a y1 value one bf16 ulp away can take the neighbouring code
+    (the per-element bar then applies to the staged comparison)."""
     g = bf16(got_bits)
     r = bf16(ref_bits)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
@@ -75,5 +78,6 @@ def check_close(got_bits, ref_bits, mode, what=""):
         assert err <= 2e-2, (what, err)
     else:
         assert err <= 5e-3, (what, err)
-        assert maxerr <= 1e-2, (what, maxerr)
+        if max_bar:
+            assert maxerr <= 1e-2, (what, maxerr)
     return err, maxerr, exact

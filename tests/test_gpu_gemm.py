@@ -231,3 +231,35 @@ def test_decode_path_workspace_reuse():
             assert torch.equal(out, first[i]), (rep, i)
     counters = host(ws[:moe.WORKSPACE_COUNTER_BYTES].view(torch.int32))
     assert np.all(counters == 0), np.nonzero(counters)
+
+
+def test_decode_path_graph_replay():
+    """The single-launch decode path captured in a HIP graph: every replay,
+    with eager calls on the same workspace in between, gives the eager
+    result bit for bit (the launch clears its own counters, so replays need
+    no fill nodes)."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, say
+    say("decode graph replay")
+    p = decode_case("offset_swiglu")
+    q = decode_case("one_token")
+    d, e = DeviceProblem(p), DeviceProblem(q)
+    n = max(moe.workspace_size(r.M, r.H, r.I, r.top_k, r.num_local_experts, 16, r.mode) for r in (p, q))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    want = d.forward(tile=16, workspace=ws)
+    want_q = e.forward(tile=16, workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(want)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        d.forward(out=out, tile=16, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), rep
+        other = e.forward(tile=16, workspace=ws)  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, want_q), rep
