@@ -334,11 +334,23 @@ DEV void g1_prefetch(const RowPtr& pg, const RowPtr& pu, const LaneOff& o, Chunk
   }
 }
 
+// Issue priority by remaining work: a wavefront that has fallen behind
+// (more of its row still to stream) is served first, so the workgroups on
+// a CU finish closer together instead of strictly in launch order.
+DEV void prio_by_progress(int done, int total) {
+  const int left4 = 4 * (total - done);
+  if (left4 > 3 * total) __builtin_amdgcn_s_setprio(3);
+  else if (left4 > 2 * total) __builtin_amdgcn_s_setprio(2);
+  else if (left4 > total) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 template <int D>
 DEV void g1_run(const RowPtr& pg, const RowPtr& pu, const LaneOff& o, int nsteps, int ch, Chunk* bg, Chunk* bu,
                 const uint32_t* xs, float& ag, float& au) {
   int s0 = 0;
   for (; s0 + D < nsteps; s0 += D) {
+    prio_by_progress(s0, nsteps);
 #pragma unroll
     for (int d = 0; d < D; d++) {
       dot_chunk2(bg[d], bu[d], xs, ch + 16 * (s0 + d), ag, au);
@@ -368,6 +380,7 @@ DEV void g2_run(const RowPtr* pr, const LaneOff& o, int nflat, int ch, Chunk* b,
   static_assert(D % 4 == 0, "row of a flattened step must be d % 4");
   int f0 = 0;
   for (; f0 + D < nflat; f0 += D) {
+    prio_by_progress(f0, nflat);
 #pragma unroll
     for (int d = 0; d < D; d++) {
       const int f = f0 + d;

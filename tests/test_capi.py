@@ -133,3 +133,29 @@ def test_header_constants_match_binding():
     assert int(consts["MOE_NUM_PHASE_EVENTS"]) == moe.NUM_PHASE_EVENTS
     # the counter block leads every forward workspace
     assert moe.workspace_size(8, 1024, 512, 8, 32, 16, 0) > moe.WORKSPACE_COUNTER_BYTES
+
+
+def test_forward_accepts_the_workspace_it_asks_for():
+    """moe_forward's host checks accept exactly moe_workspace_size() bytes
+    for every launch sequence (decode path included) and reject one byte
+    less.  Run without a GPU, so the call stops at the first device step
+    with MOE_ERR_DEVICE instead of launching on placeholder pointers."""
+    import ctypes
+
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("placeholder pointers must not reach a launch on a machine with a GPU")
+    L = moe.lib()
+    buf = torch.zeros(1 << 20, dtype=torch.uint8)
+    P = ctypes.c_void_p(buf.data_ptr())
+    for (M, H, I, E, El, k, tile) in [(6, 2048, 512, 64, 8, 4, 16), (8, 6144, 2048, 256, 32, 8, 16),
+                                      (40, 256, 256, 8, 8, 2, 16), (37, 384, 256, 16, 6, 4, 64)]:
+        for fm in (moe.FINALIZE_DETERMINISTIC, moe.FINALIZE_ATOMIC):
+            n = moe.workspace_size(M, H, I, k, El, tile, 0, fm)
+            ws = torch.zeros(n + 512, dtype=torch.uint8)
+            for size, want_ws_error in ((n, False), (n - 1, True)):
+                o = moe.make_opts(tile=tile, finalize_mode=fm)
+                o.workspace = ws.data_ptr() + (-ws.data_ptr()) % 256
+                o.workspace_bytes = size
+                st = L.moe_forward(P, None, P, P, P, P, P, P, P, P, E, k, El, 0, 0, P, M, H, I, ctypes.byref(o), None)
+                assert (st == 3) == want_ws_error, (M, H, I, tile, fm, size, st)

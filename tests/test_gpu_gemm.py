@@ -159,15 +159,15 @@ def takes_decode_path(p, tile=16):
 
 def decode_case(case):
     if case == "no_local_routes":
-        wl = synth.small_workload(oracle.W4A16, 6, 1024, 512, 64, 8, 4, 51, offset=8)
+        wl = synth.small_workload(oracle.W4A16, 6, 2048, 512, 64, 8, 4, 51, offset=8)
         raw = synth.make_raw(wl)
         raw.topk_ids[:] = np.where(raw.topk_ids < 16, raw.topk_ids + 16, raw.topk_ids)
     elif case == "hot_experts":
         # 40 routes per expert: three tiles each, the last one ragged
-        wl = synth.small_workload(oracle.W4A16, 40, 1024, 1024, 2, 2, 2, 52)
+        wl = synth.small_workload(oracle.W4A16, 40, 2048, 1024, 2, 2, 2, 52)
         raw = synth.make_raw(wl)
     elif case == "one_token":
-        wl = synth.small_workload(oracle.W4A16, 1, 1024, 512, 16, 16, 4, 53)
+        wl = synth.small_workload(oracle.W4A16, 1, 2048, 512, 16, 16, 4, 53)
         raw = synth.make_raw(wl)
     else:  # "offset_swiglu": a local window of the experts, clamped SwiGLU
         wl = synth.small_workload(oracle.W4A16, 9, 2048, 1536, 64, 16, 6, 54, offset=24, swiglu_limit=0.4,
