@@ -247,7 +247,8 @@ int moe_default_tile(int M, int top_k, int num_local_experts, moe_quant_mode_t m
   const int64_t per_expert = (int64_t)M * top_k / (num_local_experts > 0 ? num_local_experts : 1);
   if (per_expert <= 16) return 16;
   if (per_expert <= 64) return 32;
-  return 64;
+  if (per_expert <= 256) return 64;
+  return 128;
 }
 
 static_assert(MOE_WORKSPACE_COUNTER_BYTES == DEC_COUNTER_BYTES, "counter block size in moe.h");

@@ -49,6 +49,12 @@ struct Gemm2Params {
 hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream);
 hipError_t launch_gemm2(const Gemm2Params& p, hipStream_t stream);
 
+// wide-tile kernels for 128-slot tiles (prefill-sized batches, W4A16 / W4A4)
+bool wide_supported1(const Gemm1Params& p);
+bool wide_supported2(const Gemm2Params& p);
+hipError_t launch_gemm1_wide(const Gemm1Params& p, hipStream_t stream);
+hipError_t launch_gemm2_wide(const Gemm2Params& p, hipStream_t stream);
+
 // weight-streaming kernels for 16-slot tiles (decode-sized batches)
 bool stream_supported(int mode, const moe_plan_t* plan, int H, int I);
 hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream);

@@ -21,6 +21,9 @@ CASES = {
                                                swiglu_limit=0.5)),
     "w4a4_basic": (oracle.W4A4, dict(M=40, H=256, I=256, E=8, El=8, k=2, seed=44)),
     "w4a4_offset": (oracle.W4A4, dict(M=33, H=384, I=128, E=12, El=5, k=3, seed=45, offset=7)),
+    # 128-slot tiles: full tiles and ragged tails of every height
+    "w4a16_tall": (oracle.W4A16, dict(M=500, H=512, I=256, E=8, El=8, k=2, seed=50, router_bias_std=0.5)),
+    "w4a4_tall": (oracle.W4A4, dict(M=450, H=256, I=384, E=6, El=6, k=3, seed=53, router_bias_std=0.7)),
     "mx_basic": (oracle.MXFP8_MXFP4, dict(M=40, H=256, I=256, E=8, El=8, k=2, seed=46)),
     "mx_offset": (oracle.MXFP8_MXFP4, dict(M=45, H=512, I=256, E=16, El=6, k=4, seed=47, offset=9)),
 }
@@ -49,7 +52,7 @@ def y1_values(mode, q, sf):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("tile", [16, 64])
+@pytest.mark.parametrize("tile", [16, 64, 128])
 def test_gemm1_and_gemm2_stages(name, tile):
     import torch
 
