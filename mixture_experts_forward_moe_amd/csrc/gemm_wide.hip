@@ -7,14 +7,17 @@
 // exact in bf16 and fp32 accumulation; GEMM2 y2 = alpha2[e] * y1 W2[e]^T.
 //
 // Why a second shape: with bf16 activations the E2M1 weights have to be
-// decoded to bf16 on the vector ALU before an MFMA can use them (four VALU
-// instructions per pair of codes), so the ratio of decode work to MFMA work
-// is set by how many slots reuse one decoded fragment.  Here each wavefront
-// keeps all 128 slots of a tile against 64 weight rows in its accumulators
-// (8 x 4 tiles of 16 x 16), so a decoded fragment feeds up to 8 MFMAs and
-// the decode costs about half the MFMA time.  The 16-slot row groups that
-// hold no route are skipped whole: the tile's used height picks one of
-// eight unrolled bodies.
+// decoded to bf16 on the vector ALU before an MFMA can use them (16 VALU
+// instructions per 8 codes), so the ratio of decode work to MFMA work is set
+// by how many slots reuse one decoded fragment.  Here each wavefront keeps
+// all 128 slots of a tile against 64 weight rows in its accumulators (8 x 4
+// tiles of 16 x 16), so a decoded fragment feeds up to 8 MFMAs.  The decode
+// is interleaved with the MFMAs of the same wavefront (MFMA and VALU
+// overlap far better inside one instruction stream than across wavefronts):
+// a stage runs in two halves, the MFMAs of weight-row groups 0, 1 while
+// groups 2, 3 are decoded, then those of groups 2, 3 while groups 0, 1 of
+// the next stage are decoded.  The 16-slot row groups that hold no route are
+// skipped whole: the tile's used height picks one of eight unrolled bodies.
 //
 //  - workgroup: 4 wavefronts, one 128-slot tile x 256 weight rows.  GEMM1:
 //    128 gate rows j0.. and the 128 matching up rows I+j0.., wavefront w
@@ -22,7 +25,8 @@
 //    sit in one lane.  GEMM2: output columns n0+64w...
 //  - Operands are staged through registers: every thread loads its share
 //    of a stage with 16-byte loads two stages before the stage is used and
-//    writes it to LDS one stage before.  Activations come in 32-K stages
+//    writes it to LDS one stage before.  Codes and scales are staged by the
+//    wavefront that uses them, so only the activations need the barrier.  Activations come in 32-K stages
 //    (2-slot LDS ring), codes in 128-K groups of 64 bytes per weight row and
 //    their scales in 8-byte pieces (2-slot rings), a group written a quarter
 //    per stage during the group before it.  52 KiB of LDS, two workgroups
@@ -118,14 +122,15 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
   };
   const uint8_t* Wb = a.W + (int64_t)e * a.rows_per_expert * (a.K / 2);
   const uint8_t* Sb = a.W_sf + (int64_t)e * a.rows_per_expert * (a.K / 16);
-  // codes: quarter qq of a group is group chunk j = 256 qq + tid, row j >> 2,
-  // logical chunk (j & 3) ^ sb(row); scales: row tid, 8 bytes
+  // codes and scales are staged by the wavefront that uses them (its 64
+  // weight rows), so they need no workgroup barrier.  Code quarter qq of a
+  // group: lane l writes row 64 wave + 16 qq + l / 4, physical chunk l & 3
+  // (logical chunk (l & 3) ^ sb(row)); scales: row tid, 8 bytes.
   uint32_t b_off[4];
 #pragma unroll
   for (int qq = 0; qq < 4; qq++) {
-    const int j = 256 * qq + tid;
-    const int row = j >> 2;
-    const int c = (j & 3) ^ sb(row);
+    const int row = 64 * wave + 16 * qq + (lane >> 2);
+    const int c = (lane & 3) ^ sb(row);
     b_off[qq] = (uint32_t)wrow(row) * (uint32_t)(a.K / 2) + (uint32_t)c * 16u;
   }
   uint32_t s_off = (uint32_t)wrow(tid) * (uint32_t)(a.K / 16);
@@ -163,7 +168,7 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
     for (int i = 0; i < 2; i++) As[256 * i + tid] = r[i];
   };
   auto store_b = [&](int qq, int gslot) {
-    reinterpret_cast<u32x4_t*>(smem + B_OFF + gslot * B_GROUP)[256 * qq + tid] = rb[qq & 1];
+    reinterpret_cast<u32x4_t*>(smem + B_OFF + gslot * B_GROUP)[256 * wave + 64 * qq + lane] = rb[qq & 1];
   };
   auto store_s = [&](int gslot) { reinterpret_cast<uint2*>(smem + S_OFF + gslot * S_GROUP)[tid] = rs; };
 
@@ -174,29 +179,41 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
     for (int n = 0; n < 4; n++) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int a_lane = r16 * (AK * 2) + ((q ^ sa(r16)) << 4);
-  // stage t of group g, activations in ring slot t & 1
-  auto compute = [&](int t, int g) {
+  // this lane's code dword and scale of weight-row group n at stage t of
+  // group g (rows 64 wave + 16 n + r16, K [8q, 8q + 8) of the stage)
+  const int b_lane = (64 * wave + r16) * 64 + 4 * q;
+  const int b_sw = sb(r16);
+  const int s_lane = (64 * wave + r16) * 8 + (q >> 1);
+  auto decode = [&](int t, int g, int n) -> bf16x8_t {
+    const uint8_t* Bs = smem + B_OFF + (g & 1) * B_GROUP + b_lane + n * 16 * 64 + ((t ^ b_sw) << 4);
+    const uint8_t* Ss = smem + S_OFF + (g & 1) * S_GROUP + s_lane + n * 16 * 8 + 2 * t;
+    return e2m1x8_scaled_to_bf16(*reinterpret_cast<const uint32_t*>(Bs),
+                                 __builtin_amdgcn_cvt_f32_fp8((int)*Ss, 0));
+  };
+  // Stage t of group g in two halves: the MFMAs of weight-row groups 0, 1
+  // run while groups 2, 3 of this stage are decoded, those of groups 2, 3
+  // while groups 0, 1 of the next stage (tn of group gn) are decoded.
+  // Activation fragments are read from LDS once per half.
+  bf16x8_t bf[4];
+  auto compute = [&](int t, int g, int tn, int gn) {
     const uint8_t* As = smem + (t & 1) * A_STAGE + a_lane;
-    const uint8_t* Bs = smem + B_OFF + (g & 1) * B_GROUP;
-    const uint8_t* Ss = smem + S_OFF + (g & 1) * S_GROUP;
-    bf16x8_t bf[4];
 #pragma unroll
-    for (int n = 0; n < 4; n++) {
-      const int col = 64 * wave + 16 * n + r16;
-      const uint32_t cw = *reinterpret_cast<const uint32_t*>(Bs + col * 64 + ((t ^ sb(col)) << 4) + 4 * q);
-      const float sc = __builtin_amdgcn_cvt_f32_fp8((int)Ss[col * 8 + 2 * t + (q >> 1)], 0);
-      bf[n] = e2m1x8_scaled_to_bf16(cw, sc);
-    }
-    // activation fragments are read one MFMA group ahead of their use
-    bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(As);
+    for (int h = 0; h < 2; h++) {
+      bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(As);
 #pragma unroll
-    for (int m = 0; m < MTV; m++) {
-      bf16x8_t nf = af;
-      if (m + 1 < MTV) nf = *reinterpret_cast<const bf16x8_t*>(As + (m + 1) * 16 * AK * 2);
-#pragma unroll
-      for (int n = 0; n < 4; n++)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[n], acc[m][n], 0, 0, 0);
-      af = nf;
+      for (int m = 0; m < MTV; m++) {
+        bf16x8_t nf = af;
+        if (m + 1 < MTV) nf = *reinterpret_cast<const bf16x8_t*>(As + (m + 1) * 16 * AK * 2);
+        acc[m][2 * h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[2 * h], acc[m][2 * h], 0, 0, 0);
+        acc[m][2 * h + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[2 * h + 1], acc[m][2 * h + 1], 0, 0, 0);
+        if (m == 0) {
+          if (h == 0) bf[2] = decode(t, g, 2); else bf[0] = decode(tn, gn, 0);
+        }
+        if (m == (MTV > 1 ? 1 : 0)) {
+          if (h == 0) bf[3] = decode(t, g, 3); else bf[1] = decode(tn, gn, 1);
+        }
+        af = nf;
+      }
     }
   };
 
@@ -217,6 +234,8 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
   load_b(1, 1);
   load_s(1);
   __syncthreads();
+  bf[0] = decode(0, 0, 0);
+  bf[1] = decode(0, 0, 1);
 
   // ---- main loop, one code group (4 stages) per trip.  At stage s = 4g + t:
   // write stage s+1 (loaded at s-2) and code quarter t of group g+1 (loaded
@@ -240,7 +259,7 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
         store_s((g + 1) & 1);
         load_s(g + 2);
       }
-      compute(t, g);
+      compute(t, g, (t + 1) & 3, t == 3 ? g + 1 : g);
       // only global loads may move across stages: interleaving the MFMAs of
       // two stages renames the accumulators and runs out of registers
       __builtin_amdgcn_sched_barrier(0x0010);
