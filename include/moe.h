@@ -246,9 +246,11 @@ size_t moe_workspace_size(int M, int H, int I, int top_k, int num_local_experts,
  * Enqueues moe_sort, moe_grouped_gemm1_swiglu, moe_grouped_gemm2 and (in
  * deterministic mode) moe_finalize; in atomic mode with accumulate = 0 the
  * output is zero-filled first by a kernel.  Decode-sized W4A16 batches
- * (tile 16, M * top_k <= 1024, H a multiple of 1024 and at most 65536,
- * I a multiple of 512) take a single persistent launch instead that does
- * all four steps; its finalize is the deterministic one in either mode.
+ * (tile 16, M * top_k <= 1024, H and I multiples of 512, I <= 8192, and
+ * the routing plan plus one bf16 row of H within 64 KiB of LDS) take two launches
+ * instead: GEMM1 with the routing plan, then GEMM2 whose last workgroup per
+ * 64 output columns applies the finalize; that finalize is the
+ * deterministic one in either mode.
  * `out` is this GPU's share: the sum over its local routes only. */
 moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk_ids, const float* topk_weights,
                          const uint8_t* w1, const uint8_t* w1_sf, const float* w1_alpha, const uint8_t* w2,

@@ -328,7 +328,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
     return MOE_OK;
   }
   if (dec) {
-    // decode-sized batch: plan, GEMM1, GEMM2 and finalize in one launch
+    // decode-sized batch: GEMM1 (with the routing plan), then GEMM2 with the finalize
     DecodeParams d;
     d.topk_ids = topk_ids;
     d.local_expert_offset = local_expert_offset;
