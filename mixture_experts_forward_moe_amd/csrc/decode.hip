@@ -7,9 +7,11 @@
 //  dec_gemm1: every workgroup builds the batch's routing plan in LDS
 //    (per-expert counts, 16-slot tiles, stable slots in route order: the
 //    plan moe_sort builds, so there is no separate sort launch), picks its
-//    tiles, stages the tile's token rows of x in LDS and streams 16 gate +
-//    16 up weight rows of the tile's expert (expert scale, SwiGLU, bf16
-//    y1).  Workgroup (0, 0) writes the plan out.
+//    tiles, stages the tile's token rows of x in LDS and streams 32 gate +
+//    32 up weight rows of the tile's expert in two passes of 16 (expert
+//    scale, SwiGLU, bf16 y1).  Its first weight loads go out as soon as the
+//    tile's expert is known, before the slots and x are.  Workgroup (0, 0)
+//    writes the plan out.
 //  dec_gemm2: reads that plan; a workgroup streams 64 rows of W2 for a tile
 //    against the tile's y1 rows and writes y2.  The last workgroup of a
 //    column group applies the deterministic route-order finalize to those
@@ -112,9 +114,12 @@ DEV int dec_scan(int* v, int n, int* tmp) {
   return total;
 }
 
-// The batch's plan in LDS: counts, tile bases, and every route's slot
-// (slots of expert e start at 16 * tbase[e], in ascending route order).
-DEV int build_plan(const DecArgs& a, const LocalPlan& P) {
+// The batch's plan in LDS, in two parts.  plan_counts: per-expert counts and
+// tile bases (slots of expert e start at 16 * tbase[e]), which is all a
+// workgroup needs to find its tile's expert; it leaves the route ids in
+// e2p.  plan_slots: every route's slot, in ascending route order within its
+// expert.
+DEV int plan_counts(const DecArgs& a, const LocalPlan& P) {
   const int R = a.M * a.top_k;
   const int tid = threadIdx.x;
   for (int e = tid; e < a.El; e += DEC_THREADS) P.cnt[e] = 0;
@@ -131,7 +136,13 @@ DEV int build_plan(const DecArgs& a, const LocalPlan& P) {
   if (tid == 0) P.tbase[a.El] = nt;
   for (int e = tid; e < a.El; e += DEC_THREADS) P.run[e] = P.tbase[e] * DEC_T;
   __syncthreads();
-  // stable slots: wavefront 0 walks the routes 64 at a time
+  return nt;
+}
+
+// stable slots: wavefront 0 walks the routes 64 at a time
+DEV void plan_slots(const DecArgs& a, const LocalPlan& P) {
+  const int R = a.M * a.top_k;
+  const int tid = threadIdx.x;
   if (tid < 64) {
     const int lane = tid;
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -156,7 +167,6 @@ DEV int build_plan(const DecArgs& a, const LocalPlan& P) {
     }
   }
   __syncthreads();
-  return nt;
 }
 
 // expert of tile pt: the last expert whose first tile is <= pt
@@ -284,43 +294,52 @@ DEV float sum16(float v) {
   return v;
 }
 
-// Streams one gate row (and, for GEMM1, the matching up row) of K over the
-// lane's chunks and accumulates NR activation rows.  D K-steps of loads stay
-// in flight: the steady-state loop issues every load unconditionally (D
-// divides the step count) so the compiler waits only for the step it is
-// about to use, never for the whole batch.
-template <int NR, bool GATED, int D>
-DEV void stream_rows(const uint8_t* W, const uint8_t* Wsf, int64_t rg, int64_t ru, int K, int ch,
-                     const uint32_t* xs, int xsw, float* ag, float* au) {
-  const int NS = K / 512;  // a multiple of D
-  Chunk bg[D], bu[D];
+// GEMM1's stream: a lane's gate and up rows g, u (pass 0), then g + 16,
+// u + 16 (pass 1), over its chunks of K.  D K-steps of loads stay in flight
+// and the caller issues the first D before staging the activations, so
+// their latency overlaps the staging; pass 0's last D loads are pass 1's
+// first steps.  Every load in the loop is unconditional (D divides the
+// step count), so the compiler waits only for the step it is about to use.
+template <int D>
+DEV void prefetch_pairs(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t u, int K, int ch, Chunk* bg,
+                        Chunk* bu) {
 #pragma unroll
   for (int d = 0; d < D; d++) {
-    bg[d] = load_chunk(W, Wsf, rg, K, ch + 16 * d);
-    if (GATED) bu[d] = load_chunk(W, Wsf, ru, K, ch + 16 * d);
+    bg[d] = load_chunk(W, Wsf, g, K, ch + 16 * d);
+    bu[d] = load_chunk(W, Wsf, u, K, ch + 16 * d);
   }
-  int s0 = 0;
-  for (; s0 + D < NS; s0 += D) {
+}
+
+template <int D>
+DEV void stream_pairs2(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t u, int K, int ch,
+                       const uint32_t* xs, Chunk* bg, Chunk* bu, float* ag, float* au) {
+  const int NS = K / 512;  // a multiple of D
 #pragma unroll
-    for (int d = 0; d < D; d++) {
-      const int kc = ch + 16 * (s0 + d);
-      if (GATED) dot_chunk2<NR>(bg[d], bu[d], xs, xsw, kc, ag, au);
-      else dot_chunk<NR>(bg[d], xs, xsw, kc, ag);
-      bg[d] = load_chunk(W, Wsf, rg, K, kc + 16 * D);
-      if (GATED) bu[d] = load_chunk(W, Wsf, ru, K, kc + 16 * D);
-      __builtin_amdgcn_sched_barrier(0);  // keep one step's values live at a time
+  for (int p = 0; p < 2; p++) {
+    const int64_t gp = g + 16 * p, up = u + 16 * p;
+    const int end = p == 0 ? NS : NS - D;  // pass 1's last D steps load nothing
+    for (int s0 = 0; s0 < end; s0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; d++) {
+        dot_chunk2<1>(bg[d], bu[d], xs, 0, ch + 16 * (s0 + d), &ag[p], &au[p]);
+        const int sn = s0 + d + D;
+        const bool wrap = sn >= NS;  // pass 0 only: the next loads are pass 1's
+        const int kn = ch + 16 * (wrap ? sn - NS : sn);
+        bg[d] = load_chunk(W, Wsf, wrap ? gp + 16 : gp, K, kn);
+        bu[d] = load_chunk(W, Wsf, wrap ? up + 16 : up, K, kn);
+        __builtin_amdgcn_sched_barrier(0);  // keep one step's values live at a time
+      }
     }
   }
 #pragma unroll
-  for (int d = 0; d < D; d++) {
-    const int kc = ch + 16 * (s0 + d);
-    if (GATED) dot_chunk2<NR>(bg[d], bu[d], xs, xsw, kc, ag, au);
-    else dot_chunk<NR>(bg[d], xs, xsw, kc, ag);
-  }
+  for (int d = 0; d < D; d++) dot_chunk2<1>(bg[d], bu[d], xs, 0, ch + 16 * (NS - D + d), &ag[1], &au[1]);
 }
 
 // ---------------------------------------------------------------- GEMM1
 
+// Workgroup (bx, y) computes y1 columns 32 bx .. 32 bx + 31 (16 per pass)
+// of tiles y, y + gridDim.y, ...; wavefront w, lane (rr, ch) owns column
+// 32 bx + 16 p + 4 w + rr of pass p.
 template <int D>
 __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
@@ -332,19 +351,67 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
   P.tmp = P.run + a.El;
   P.e2p = P.tmp + DEC_THREADS / 64;
   int* rows = P.e2p + R;  // [16] routes of this tile
-  // x rows at the next 16-byte boundary; offset arithmetic on the LDS array
-  // itself (an integer round trip would turn every read into a flat load,
-  // and flat loads make each step wait for all weight loads in flight)
+  // the x row at the next 16-byte boundary; offset arithmetic on the LDS
+  // array itself (an integer round trip would turn every read into a flat
+  // load, and flat loads make each step wait for all weight loads in flight)
   const int xs_word = (3 * a.El + 1 + DEC_THREADS / 64 + R + DEC_T + 3) & ~3;
-  uint32_t* xs = dsm + xs_word;  // [DEC_ROWS][H/2]
-  const int xsw = a.H / 2;
+  uint32_t* xs = dsm + xs_word;  // [H/2]
 
-  const int nt = build_plan(a, P);
+  const int nt = plan_counts(a, P);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rr = lane >> 4, ch = lane & 15;
+  const int col = 32 * blockIdx.x + 4 * wave + rr;
+  bool slots_done = false;
+
+  for (int pt = blockIdx.y; pt < nt; pt += gridDim.y) {
+    const int e = tile_owner(P, a.El, pt);
+    const int slot0 = pt * DEC_T;
+    const int valid = min(DEC_T, P.tbase[e] * DEC_T + P.cnt[e] - slot0);
+    const int64_t rg = (int64_t)e * 2 * a.I + col;
+    const int64_t ru = rg + a.I;
+    const float al = a.w1_alpha[e];
+    for (int r0 = 0; r0 < valid; r0++) {
+      Chunk bg[D], bu[D];
+      prefetch_pairs<D>(a.w1, a.w1_sf, rg, ru, a.H, ch, bg, bu);
+      if (!slots_done) {
+        plan_slots(a, P);
+        slots_done = true;
+      }
+      if (r0 == 0) {
+        if (tid < DEC_T) rows[tid] = -1;
+        __syncthreads();
+        for (int r = tid; r < R; r += DEC_THREADS) {
+          const int s = P.e2p[r];
+          if (s >= slot0 && s < slot0 + DEC_T) rows[s - slot0] = r;
+        }
+        __syncthreads();
+      }
+      // stage the route's token row of x
+      {
+        const int64_t tok = rows[r0] / a.top_k;
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.x + tok * a.x_row_stride);
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs);
+        for (int i = tid; i < a.H / 8; i += DEC_THREADS) dst[i] = src[i];
+      }
+      __syncthreads();
+      float ag[2] = {0.0f, 0.0f}, au[2] = {0.0f, 0.0f};
+      stream_pairs2<D>(a.w1, a.w1_sf, rg, ru, a.H, ch, xs, bg, bu, ag, au);
+#pragma unroll
+      for (int p = 0; p < 2; p++) {
+        const float g = sum16(ag[p]);
+        const float u = sum16(au[p]);
+        if (ch == 0) {
+          const float y = swiglu_f32(g * al, u * al, a.sw_alpha, a.sw_beta, a.sw_limit);
+          a.y1[(int64_t)(slot0 + r0) * a.I + col + 16 * p] = f32_to_bf16(y);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (!slots_done) plan_slots(a, P);
 
   if (blockIdx.x == 0 && blockIdx.y == 0) {
-    // the plan, for the record and for callers that read it
+    // the plan, for the record and for GEMM2
     for (int r = tid; r < R; r += DEC_THREADS) a.e2p[r] = P.e2p[r];
     for (int64_t s = tid; s < a.slots; s += DEC_THREADS) a.p2e[s] = -1;
     for (int i = tid; i < a.max_tiles; i += DEC_THREADS) {
@@ -368,46 +435,6 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
     for (int r = tid; r < R; r += DEC_THREADS)
       if (P.e2p[r] >= 0) a.p2e[P.e2p[r]] = r;
   }
-
-  for (int pt = blockIdx.y; pt < nt; pt += gridDim.y) {
-    const int e = tile_owner(P, a.El, pt);
-    const int slot0 = pt * DEC_T;
-    const int valid = min(DEC_T, P.tbase[e] * DEC_T + P.cnt[e] - slot0);
-    if (tid < DEC_T) rows[tid] = -1;
-    __syncthreads();
-    for (int r = tid; r < R; r += DEC_THREADS) {
-      const int s = P.e2p[r];
-      if (s >= slot0 && s < slot0 + DEC_T) rows[s - slot0] = r;
-    }
-    __syncthreads();
-    const int64_t rg = (int64_t)e * 2 * a.I + 16 * blockIdx.x + 4 * wave + rr;
-    const int64_t ru = rg + a.I;
-    const float al = a.w1_alpha[e];
-    for (int r0 = 0; r0 < valid; r0 += DEC_ROWS) {
-      const int nr = min(DEC_ROWS, valid - r0);
-      // stage the pass's token rows of x
-      for (int t = 0; t < nr; t++) {
-        const int64_t tok = rows[r0 + t] / a.top_k;
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.x + tok * a.x_row_stride);
-        u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + t * xsw);
-        for (int i = tid; i < a.H / 8; i += DEC_THREADS) dst[i] = src[i];
-      }
-      __syncthreads();
-      float ag[DEC_ROWS] = {}, au[DEC_ROWS] = {};
-      stream_rows<DEC_ROWS, true, D>(a.w1, a.w1_sf, rg, ru, a.H, ch, xs, xsw, ag, au);
-      const int col = 16 * blockIdx.x + 4 * wave + rr;
-#pragma unroll
-      for (int t = 0; t < DEC_ROWS; t++) {
-        const float g = sum16(ag[t]);
-        const float u = sum16(au[t]);
-        if (ch == 0 && t < nr) {
-          const float y = swiglu_f32(g * al, u * al, a.sw_alpha, a.sw_beta, a.sw_limit);
-          a.y1[(int64_t)(slot0 + r0 + t) * a.I + col] = f32_to_bf16(y);
-        }
-      }
-      __syncthreads();
-    }
-  }
 }
 
 // ---------------------------------------------------------------- GEMM2
@@ -415,14 +442,19 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
 // One lane's share of 16 rows x K: rows 4g + rr (g = 0..3), chunks ch + 16 s.
 // The four row groups are streamed interleaved (flattened index f: group
 // f % 4, step f / 4) so that all their loads are in flight together; D
-// divides the 4 * K/512 flattened steps and every load is unconditional.
-template <int NR, int D>
-DEV void stream_rows16(const uint8_t* W, const uint8_t* Wsf, int64_t row0, int K, int ch, const uint32_t* xs,
-                       int xsw, float (*acc)[DEC_ROWS]) {
-  const int total = 4 * (K / 512);
-  Chunk b[D];
+// divides the 4 * K/512 flattened steps and every load in the loop is
+// unconditional.  The caller issues the first D loads (prefetch16) before
+// staging the activations.
+template <int D>
+DEV void prefetch16(const uint8_t* W, const uint8_t* Wsf, int64_t row0, int K, int ch, Chunk* b) {
 #pragma unroll
   for (int d = 0; d < D; d++) b[d] = load_chunk(W, Wsf, row0 + 4 * (d & 3), K, ch + 16 * (d >> 2));
+}
+
+template <int NR, int D>
+DEV void stream_rows16(const uint8_t* W, const uint8_t* Wsf, int64_t row0, int K, int ch, const uint32_t* xs,
+                       int xsw, Chunk* b, float (*acc)[DEC_ROWS]) {
+  const int total = 4 * (K / 512);
   int f0 = 0;
   for (; f0 + D < total; f0 += D) {
 #pragma unroll
@@ -517,6 +549,8 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm2_kernel(const DecArgs a)
     const int64_t row0 = (int64_t)e * a.H + c0 + 16 * wave + rr;
     for (int r0 = 0; r0 < valid; r0 += DEC_ROWS) {
       const int nr = min(DEC_ROWS, valid - r0);
+      Chunk b[D];
+      prefetch16<D>(a.w2, a.w2_sf, row0, a.I, ch, b);
       __syncthreads();
       for (int t = 0; t < nr; t++) {
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.y1 + (int64_t)(slot0 + r0 + t) * a.I);
@@ -525,7 +559,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm2_kernel(const DecArgs a)
       }
       __syncthreads();
       float acc[4][DEC_ROWS] = {};
-      stream_rows16<DEC_ROWS, D>(a.w2, a.w2_sf, row0, a.I, ch, xs, xsw, acc);
+      stream_rows16<DEC_ROWS, D>(a.w2, a.w2_sf, row0, a.I, ch, xs, xsw, b, acc);
 #pragma unroll
       for (int g = 0; g < 4; g++)
 #pragma unroll
@@ -603,16 +637,15 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const size_t lds1 = plan_lds(a.El, R) + sizeof(uint16_t) * DEC_ROWS * a.H + 16;
   // prefetch depth: the deepest that divides the K-step count
   const int ns1 = a.H / 512, ns2 = 4 * (a.I / 512);
-  const dim3 g1(a.I / 16, P), g2(a.H / 64, P);
+  const dim3 g1(a.I / 32, P), g2(a.H / 64, P);
   if (p.mark) p.mark(p.mark_ctx, 1);
-  if (ns1 % 6 == 0) dec_gemm1_kernel<6><<<g1, DEC_THREADS, lds1, stream>>>(a);
-  else if (ns1 % 4 == 0) dec_gemm1_kernel<4><<<g1, DEC_THREADS, lds1, stream>>>(a);
+  if (ns1 % 4 == 0) dec_gemm1_kernel<4><<<g1, DEC_THREADS, lds1, stream>>>(a);
   else if (ns1 % 2 == 0) dec_gemm1_kernel<2><<<g1, DEC_THREADS, lds1, stream>>>(a);
   else dec_gemm1_kernel<1><<<g1, DEC_THREADS, lds1, stream>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.mark) p.mark(p.mark_ctx, 2);
-  if (ns2 % 8 == 0) dec_gemm2_kernel<8><<<g2, DEC_THREADS, 0, stream>>>(a);
+  if (ns2 % 4 == 0) dec_gemm2_kernel<4><<<g2, DEC_THREADS, 0, stream>>>(a);
   else dec_gemm2_kernel<4><<<g2, DEC_THREADS, 0, stream>>>(a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
