@@ -37,6 +37,15 @@
 
 namespace moe {
 
+// A workgroup barrier that orders LDS accesses only: global loads and
+// stores in flight stay in flight (a full __syncthreads waits for all of
+// them, which would drain the weight stream at every barrier).
+DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_ROWS = 1;        // activation rows per pass
 constexpr int DEC_TILE_STRIDE = 8; // workgroups per column group, looping over tiles
@@ -180,7 +189,12 @@ DEV int tile_owner(const LocalPlan& P, int El, int pt) {
   return lo;
 }
 
-// one K-step of one weight row for one lane: 32 codes + two scale codes
+// one K-step of one weight row for one lane: 32 codes + two scale codes.
+// The two scale bytes of chunk kc sit at byte 2 kc of the row's scales;
+// the lane loads the aligned 32-bit word holding them (kc and kc ^ 1
+// share it) and dot_chunk shifts the pair down for odd kc.  A 16-bit load
+// would need a zero-extension that the compiler may place where it has to
+// wait for every load in flight.  The scale rows must be 4-byte aligned.
 struct Chunk {
   u32x4_t w;
   uint32_t s;
@@ -189,9 +203,11 @@ struct Chunk {
 DEV Chunk load_chunk(const uint8_t* W, const uint8_t* Wsf, int64_t row, int K, int kc) {
   Chunk c;
   c.w = *reinterpret_cast<const u32x4_t*>(W + row * (K / 2) + (int64_t)kc * 16);
-  c.s = *reinterpret_cast<const uint16_t*>(Wsf + row * (K / 16) + (int64_t)kc * 2);
+  c.s = *reinterpret_cast<const uint32_t*>(Wsf + row * (K / 16) + (int64_t)(kc & ~1) * 2);
   return c;
 }
+
+DEV uint32_t chunk_scales(const Chunk& c, int kc) { return c.s >> (16 * (kc & 1)); }
 
 // two E2M1 codes (byte B of w) as a bf16 pair, exact
 template <int B>
@@ -210,8 +226,9 @@ DEV void dot_chunk(const Chunk& c, const uint32_t* xs, int x_stride_words, int k
     wb[4 * j + 2] = e2m1x2_bf16<2>(c.w[j]);
     wb[4 * j + 3] = e2m1x2_bf16<3>(c.w[j]);
   }
-  const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)c.s, 0);
-  const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)c.s, 1);
+  const int sc = (int)chunk_scales(c, kc);
+  const float s0 = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
+  const float s1 = __builtin_amdgcn_cvt_f32_fp8(sc, 1);
 #pragma unroll
   for (int t = 0; t < NR; t++) {
     // activation pairs as scalars (bit-casting an element of a vector
@@ -257,8 +274,9 @@ DEV void dot_chunk2(const Chunk& cg, const Chunk& cu, const uint32_t* xs, int x_
     wu[4 * j + 2] = e2m1x2_bf16<2>(cu.w[j]);
     wu[4 * j + 3] = e2m1x2_bf16<3>(cu.w[j]);
   }
-  const float g0 = __builtin_amdgcn_cvt_f32_fp8((int)cg.s, 0), g1 = __builtin_amdgcn_cvt_f32_fp8((int)cg.s, 1);
-  const float u0 = __builtin_amdgcn_cvt_f32_fp8((int)cu.s, 0), u1 = __builtin_amdgcn_cvt_f32_fp8((int)cu.s, 1);
+  const int gs = (int)chunk_scales(cg, kc), us = (int)chunk_scales(cu, kc);
+  const float g0 = __builtin_amdgcn_cvt_f32_fp8(gs, 0), g1 = __builtin_amdgcn_cvt_f32_fp8(gs, 1);
+  const float u0 = __builtin_amdgcn_cvt_f32_fp8(us, 0), u1 = __builtin_amdgcn_cvt_f32_fp8(us, 1);
 #pragma unroll
   for (int t = 0; t < NR; t++) {
     const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(xs + t * x_stride_words + kc * 16);
@@ -307,6 +325,7 @@ DEV void prefetch_pairs(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t
   for (int d = 0; d < D; d++) {
     bg[d] = load_chunk(W, Wsf, g, K, ch + 16 * d);
     bu[d] = load_chunk(W, Wsf, u, K, ch + 16 * d);
+    __builtin_amdgcn_sched_barrier(0);  // issue in the stream loop's order
   }
 }
 
@@ -448,7 +467,10 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
 template <int D>
 DEV void prefetch16(const uint8_t* W, const uint8_t* Wsf, int64_t row0, int K, int ch, Chunk* b) {
 #pragma unroll
-  for (int d = 0; d < D; d++) b[d] = load_chunk(W, Wsf, row0 + 4 * (d & 3), K, ch + 16 * (d >> 2));
+  for (int d = 0; d < D; d++) {
+    b[d] = load_chunk(W, Wsf, row0 + 4 * (d & 3), K, ch + 16 * (d >> 2));
+    __builtin_amdgcn_sched_barrier(0);  // issue in the stream loop's order
+  }
 }
 
 template <int NR, int D>
@@ -502,83 +524,141 @@ DEV int publish_bump(int* c) {
   return old;
 }
 
+// out[m, col], out[m, col + 1] in route order, every y2 load of the token
+// issued before the sums.  s[j], w[j]: route j's slot (or -1) and weight x
+// routed scaling factor, for the first DEC_FJ routes (any further routes
+// are read here).
+constexpr int DEC_FJ = 8;
+DEV void finalize_token(const DecArgs& a, int m, int col, const int* s, const float* w) {
+  uint32_t* o = reinterpret_cast<uint32_t*>(a.out + (int64_t)m * a.H + col);
+  const uint32_t seed = a.accumulate ? *o : 0u;
+  int sj[DEC_FJ];
+  uint32_t v[DEC_FJ];
+#pragma unroll
+  for (int j = 0; j < DEC_FJ; j++) {
+    sj[j] = s[j];
+    v[j] = sj[j] >= 0 ? ld_dev(reinterpret_cast<const uint32_t*>(a.y2 + (int64_t)sj[j] * a.H + col)) : 0u;
+  }
+  float acc0 = __uint_as_float(seed << 16), acc1 = __uint_as_float(seed & 0xffff0000u);
+#pragma unroll
+  for (int j = 0; j < DEC_FJ; j++) {
+    if (sj[j] < 0) continue;
+    acc0 = acc0 + w[j] * __uint_as_float(v[j] << 16);
+    acc1 = acc1 + w[j] * __uint_as_float(v[j] & 0xffff0000u);
+  }
+  for (int j = DEC_FJ; j < a.top_k; j++) {
+    const int r = m * a.top_k + j;
+    const int sr = a.e2p[r];
+    if (sr < 0) continue;
+    const float wf = a.topk_w[r] * a.rsf;
+    const uint32_t y = ld_dev(reinterpret_cast<const uint32_t*>(a.y2 + (int64_t)sr * a.H + col));
+    acc0 = acc0 + wf * __uint_as_float(y << 16);
+    acc1 = acc1 + wf * __uint_as_float(y & 0xffff0000u);
+  }
+  *o = pack_bf16x2(acc0, acc1);
+}
+
+// the first DEC_FJ routes of token m: slots (or -1) and scaled weights
+DEV void load_fin_routes(const DecArgs& a, int m, int* s, float* w) {
+#pragma unroll
+  for (int j = 0; j < DEC_FJ; j++) {
+    const bool ok = m < a.M && j < a.top_k;
+    const int r = ok ? m * a.top_k + j : 0;
+    s[j] = ok ? a.e2p[r] : -1;
+    w[j] = a.topk_w[r] * a.rsf;
+  }
+}
+
 // out[:, c0 : c0 + 64] in route order for every token.  Thread (tt, p) owns
-// columns c0 + 2p and c0 + 2p + 1 of tokens tt, tt + 8, ...
-DEV void finalize_cols(const DecArgs& a, int c0) {
+// columns c0 + 2p and c0 + 2p + 1 of tokens tt, tt + 8, ...; the route
+// inputs of tokens 0..7 come preloaded in LDS (fs, fw).
+DEV void finalize_cols(const DecArgs& a, int c0, const int (*fs)[DEC_FJ], const float (*fw)[DEC_FJ]) {
   const int tid = threadIdx.x;
   const int p = tid & 31, tt = tid >> 5;
   const int col = c0 + 2 * p;
-  for (int m = tt; m < a.M; m += DEC_THREADS / 32) {
-    uint32_t* o = reinterpret_cast<uint32_t*>(a.out + (int64_t)m * a.H + col);
-    float acc0 = 0.0f, acc1 = 0.0f;
-    if (a.accumulate) {
-      const uint32_t v = *o;
-      acc0 = __uint_as_float(v << 16);
-      acc1 = __uint_as_float(v & 0xffff0000u);
-    }
-    for (int j = 0; j < a.top_k; j++) {
-      const int r = m * a.top_k + j;
-      const int s = a.e2p[r];
-      if (s < 0) continue;
-      const float wf = a.topk_w[r] * a.rsf;
-      const uint32_t v = ld_dev(reinterpret_cast<const uint32_t*>(a.y2 + (int64_t)s * a.H + col));
-      acc0 = acc0 + wf * __uint_as_float(v << 16);
-      acc1 = acc1 + wf * __uint_as_float(v & 0xffff0000u);
-    }
-    *o = pack_bf16x2(acc0, acc1);
+  if (tt < a.M) finalize_token(a, tt, col, fs[tt], fw[tt]);
+  for (int m = tt + DEC_THREADS / 32; m < a.M; m += DEC_THREADS / 32) {
+    int s[DEC_FJ];
+    float w[DEC_FJ];
+    load_fin_routes(a, m, s, w);
+    finalize_token(a, m, col, s, w);
   }
 }
 
 DEV int* done_count(const DecArgs& a, int c) { return a.counters + DEC_CTR_SLOT * (1 + DEC_MAX_TILES + c); }
 
+constexpr int DEC_YMAX = 4;  // u32x4 per thread for one y1 row: I <= 8192
+
+// Workgroup (bx, y): y2 columns 64 bx .. 64 bx + 63 of tiles y, y +
+// gridDim.y, ...  Per route row: the y1 row goes into registers, the first
+// D weight steps are issued, then y1 goes to LDS (waiting for its own loads
+// only) and the stream starts.
 template <int D>
 __global__ __launch_bounds__(DEC_THREADS) void dec_gemm2_kernel(const DecArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t xs[DEC_ROWS * 8192 / 2];
-  __shared__ uint16_t ybuf[DEC_ROWS][64];
+  __shared__ __attribute__((aligned(16))) uint32_t xs[8192 / 2];
+  __shared__ uint16_t ybuf[64];
   __shared__ int last;
+  __shared__ int fs[DEC_THREADS / 32][DEC_FJ];    // finalize inputs of tokens 0..7
+  __shared__ float fw[DEC_THREADS / 32][DEC_FJ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rr = lane >> 4, ch = lane & 15;
   const int c0 = 64 * blockIdx.x;
   const int xsw = a.I / 2;
+  const int xn = a.I / 8;  // u32x4 per y1 row
+  // the tile count and this workgroup's first tile in one round of loads
+  // (the tile arrays hold max_tiles >= gridDim.y entries)
   const int nt = *a.num_tiles;
+  int te = a.tile_expert[blockIdx.y], tl = a.tile_limit[blockIdx.y];
+  if (tid < DEC_THREADS / 32 * DEC_FJ) {
+    const int m = tid / DEC_FJ, j = tid % DEC_FJ;
+    const bool ok = m < a.M && j < a.top_k;
+    const int r = ok ? m * a.top_k + j : 0;
+    fs[m][j] = ok ? a.e2p[r] : -1;
+    fw[m][j] = a.topk_w[r] * a.rsf;
+  }
   for (int pt = blockIdx.y; pt < nt; pt += gridDim.y) {
-    const int e = a.tile_expert[pt];
+    if (pt != (int)blockIdx.y) {
+      te = a.tile_expert[pt];
+      tl = a.tile_limit[pt];
+    }
+    const int e = te;
     const int slot0 = pt * DEC_T;
-    const int valid = a.tile_limit[pt] - slot0;
+    const int valid = tl - slot0;
     const float al = a.w2_alpha[e];
     const int64_t row0 = (int64_t)e * a.H + c0 + 16 * wave + rr;
-    for (int r0 = 0; r0 < valid; r0 += DEC_ROWS) {
-      const int nr = min(DEC_ROWS, valid - r0);
+    for (int r0 = 0; r0 < valid; r0++) {
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.y1 + (int64_t)(slot0 + r0) * a.I);
+      u32x4_t yv[DEC_YMAX];
+#pragma unroll
+      for (int j = 0; j < DEC_YMAX; j++) yv[j] = src[min(tid + DEC_THREADS * j, xn - 1)];
+      __builtin_amdgcn_sched_barrier(0);  // the y1 loads go out before the weight loads
       Chunk b[D];
       prefetch16<D>(a.w2, a.w2_sf, row0, a.I, ch, b);
-      __syncthreads();
-      for (int t = 0; t < nr; t++) {
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.y1 + (int64_t)(slot0 + r0 + t) * a.I);
-        u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + t * xsw);
-        for (int i = tid; i < a.I / 8; i += DEC_THREADS) dst[i] = src[i];
-      }
-      __syncthreads();
+      lds_barrier();  // the previous row's xs and ybuf are no longer read
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs);
+#pragma unroll
+      for (int j = 0; j < DEC_YMAX; j++)
+        if (tid + DEC_THREADS * j < xn) dst[tid + DEC_THREADS * j] = yv[j];
+      lds_barrier();
       float acc[4][DEC_ROWS] = {};
       stream_rows16<DEC_ROWS, D>(a.w2, a.w2_sf, row0, a.I, ch, xs, xsw, b, acc);
 #pragma unroll
-      for (int g = 0; g < 4; g++)
-#pragma unroll
-        for (int t = 0; t < DEC_ROWS; t++) {
-          const float v = sum16(acc[g][t]);
-          if (ch == 0 && t < nr) ybuf[t][16 * wave + 4 * g + rr] = f32_to_bf16(v * al);
-        }
-      __syncthreads();
-      // each row's 64 outputs: one 128-byte line from 32 lanes
-      for (int i = tid; i < nr * 32; i += DEC_THREADS)
-        st_dev(reinterpret_cast<uint32_t*>(a.y2 + (int64_t)(slot0 + r0 + i / 32) * a.H + c0) + (i & 31),
-               reinterpret_cast<const uint32_t*>(&ybuf[i / 32][0])[i & 31]);
+      for (int g = 0; g < 4; g++) {
+        const float v = sum16(acc[g][0]);
+        if (ch == 0) ybuf[16 * wave + 4 * g + rr] = f32_to_bf16(v * al);
+      }
+      lds_barrier();
+      // the row's 64 outputs: one 128-byte line from 32 lanes
+      if (tid < 32)
+        st_dev(reinterpret_cast<uint32_t*>(a.y2 + (int64_t)(slot0 + r0) * a.H + c0) + tid,
+               reinterpret_cast<const uint32_t*>(ybuf)[tid]);
     }
   }
   const int old = publish_bump(done_count(a, blockIdx.x));
   if (tid == 0) last = (old == (int)gridDim.y - 1);
   __syncthreads();
   if (last) {
-    finalize_cols(a, c0);
+    finalize_cols(a, c0, fs, fw);
     if (tid == 0) __hip_atomic_store(done_count(a, blockIdx.x), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
