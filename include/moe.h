@@ -246,8 +246,9 @@ size_t moe_workspace_size(int M, int H, int I, int top_k, int num_local_experts,
  * Enqueues moe_sort, moe_grouped_gemm1_swiglu, moe_grouped_gemm2 and (in
  * deterministic mode) moe_finalize; in atomic mode with accumulate = 0 the
  * output is zero-filled first by a kernel.  Decode-sized W4A16 batches
- * (tile 16, M * top_k <= 1024, H and I multiples of 512, I <= 8192, and
- * the routing plan plus one bf16 row of H within 64 KiB of LDS) take two launches
+ * (tile 16, M * top_k <= 1024, H and I multiples of 512, I <= 8192,
+ * 4-byte aligned w1_sf and w2_sf, and the routing plan plus one bf16 row
+ * of H within 64 KiB of LDS) take two launches
  * instead: GEMM1 with the routing plan, then GEMM2 whose last workgroup per
  * 64 output columns applies the finalize; that finalize is the
  * deterministic one in either mode.

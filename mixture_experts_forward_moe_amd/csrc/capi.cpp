@@ -313,8 +313,9 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   base += align256(y1_bytes(quant_mode, L.slots, I));
   uint8_t* y1_sf = (quant_mode == MOE_QUANT_W4A16) ? NULL : base;
   base += align256(y1_sf_bytes(quant_mode, L.slots, I));
+  // (the decode kernels read scale pairs as aligned 32-bit words)
   const bool dec = tile == 16 && decode_supported(quant_mode, M, top_k, num_local_experts, H, I) &&
-                   opts->x_row_stride % 8 == 0;
+                   opts->x_row_stride % 8 == 0 && ((uintptr_t)w1_sf & 3) == 0 && ((uintptr_t)w2_sf & 3) == 0;
   uint16_t* y2 = (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC || dec) ? (uint16_t*)base : NULL;
 
   hipStream_t st = (hipStream_t)stream;
