@@ -51,6 +51,8 @@ constexpr int DEC_ROWS = 1;        // activation rows per pass
 constexpr int DEC_TILE_STRIDE = 8; // workgroups per column group, looping over tiles
 
 constexpr int DEC_T = 16;          // plan tile
+constexpr int G1_NP = 2;           // GEMM1 passes of 16 columns per workgroup
+constexpr int G1_D = 4;            // GEMM1 K-steps in flight per lane
 
 struct DecArgs {
   const int32_t* ids;
@@ -329,20 +331,20 @@ DEV void prefetch_pairs(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t
   }
 }
 
-template <int D>
-DEV void stream_pairs2(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t u, int K, int ch,
-                       const uint32_t* xs, Chunk* bg, Chunk* bu, float* ag, float* au) {
+template <int D, int NP>
+DEV void stream_pairs(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t u, int K, int ch,
+                      const uint32_t* xs, Chunk* bg, Chunk* bu, float* ag, float* au) {
   const int NS = K / 512;  // a multiple of D
 #pragma unroll
-  for (int p = 0; p < 2; p++) {
+  for (int p = 0; p < NP; p++) {
     const int64_t gp = g + 16 * p, up = u + 16 * p;
-    const int end = p == 0 ? NS : NS - D;  // pass 1's last D steps load nothing
+    const int end = p + 1 < NP ? NS : NS - D;  // the last pass's last D steps load nothing
     for (int s0 = 0; s0 < end; s0 += D) {
 #pragma unroll
       for (int d = 0; d < D; d++) {
         dot_chunk2<1>(bg[d], bu[d], xs, 0, ch + 16 * (s0 + d), &ag[p], &au[p]);
         const int sn = s0 + d + D;
-        const bool wrap = sn >= NS;  // pass 0 only: the next loads are pass 1's
+        const bool wrap = sn >= NS;  // not the last pass: the next loads are the next pass's
         const int kn = ch + 16 * (wrap ? sn - NS : sn);
         bg[d] = load_chunk(W, Wsf, wrap ? gp + 16 : gp, K, kn);
         bu[d] = load_chunk(W, Wsf, wrap ? up + 16 : up, K, kn);
@@ -351,7 +353,8 @@ DEV void stream_pairs2(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t 
     }
   }
 #pragma unroll
-  for (int d = 0; d < D; d++) dot_chunk2<1>(bg[d], bu[d], xs, 0, ch + 16 * (NS - D + d), &ag[1], &au[1]);
+  for (int d = 0; d < D; d++)
+    dot_chunk2<1>(bg[d], bu[d], xs, 0, ch + 16 * (NS - D + d), &ag[NP - 1], &au[NP - 1]);
 }
 
 // ---------------------------------------------------------------- GEMM1
@@ -359,7 +362,7 @@ DEV void stream_pairs2(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t 
 // Workgroup (bx, y) computes y1 columns 32 bx .. 32 bx + 31 (16 per pass)
 // of tiles y, y + gridDim.y, ...; wavefront w, lane (rr, ch) owns column
 // 32 bx + 16 p + 4 w + rr of pass p.
-template <int D>
+template <int D, int NP>
 __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
   const int R = a.M * a.top_k;
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
   const int nt = plan_counts(a, P);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rr = lane >> 4, ch = lane & 15;
-  const int col = 32 * blockIdx.x + 4 * wave + rr;
+  const int col = 16 * NP * blockIdx.x + 4 * wave + rr;
   bool slots_done = false;
 
   for (int pt = blockIdx.y; pt < nt; pt += gridDim.y) {
@@ -413,10 +416,10 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
         for (int i = tid; i < a.H / 8; i += DEC_THREADS) dst[i] = src[i];
       }
       __syncthreads();
-      float ag[2] = {0.0f, 0.0f}, au[2] = {0.0f, 0.0f};
-      stream_pairs2<D>(a.w1, a.w1_sf, rg, ru, a.H, ch, xs, bg, bu, ag, au);
+      float ag[NP] = {}, au[NP] = {};
+      stream_pairs<D, NP>(a.w1, a.w1_sf, rg, ru, a.H, ch, xs, bg, bu, ag, au);
 #pragma unroll
-      for (int p = 0; p < 2; p++) {
+      for (int p = 0; p < NP; p++) {
         const float g = sum16(ag[p]);
         const float u = sum16(au[p]);
         if (ch == 0) {
@@ -716,17 +719,16 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int P = a.max_tiles < DEC_TILE_STRIDE ? (a.max_tiles > 0 ? a.max_tiles : 1) : DEC_TILE_STRIDE;
   const size_t lds1 = plan_lds(a.El, R) + sizeof(uint16_t) * DEC_ROWS * a.H + 16;
   // prefetch depth: the deepest that divides the K-step count
-  const int ns1 = a.H / 512, ns2 = 4 * (a.I / 512);
-  const dim3 g1(a.I / 32, P), g2(a.H / 64, P);
+  const int ns1 = a.H / 512;
+  const dim3 g1(a.I / (16 * G1_NP), P), g2(a.H / 64, P);
   if (p.mark) p.mark(p.mark_ctx, 1);
-  if (ns1 % 4 == 0) dec_gemm1_kernel<4><<<g1, DEC_THREADS, lds1, stream>>>(a);
-  else if (ns1 % 2 == 0) dec_gemm1_kernel<2><<<g1, DEC_THREADS, lds1, stream>>>(a);
-  else dec_gemm1_kernel<1><<<g1, DEC_THREADS, lds1, stream>>>(a);
+  if (ns1 % G1_D == 0) dec_gemm1_kernel<G1_D, G1_NP><<<g1, DEC_THREADS, lds1, stream>>>(a);
+  else if (ns1 % 2 == 0) dec_gemm1_kernel<2, G1_NP><<<g1, DEC_THREADS, lds1, stream>>>(a);
+  else dec_gemm1_kernel<1, G1_NP><<<g1, DEC_THREADS, lds1, stream>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.mark) p.mark(p.mark_ctx, 2);
-  if (ns2 % 4 == 0) dec_gemm2_kernel<4><<<g2, DEC_THREADS, 0, stream>>>(a);
-  else dec_gemm2_kernel<4><<<g2, DEC_THREADS, 0, stream>>>(a);
+  dec_gemm2_kernel<4><<<g2, DEC_THREADS, 0, stream>>>(a);  // 4 * I/512 K-steps: a multiple of 4
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.mark) p.mark(p.mark_ctx, 3);  // the finalize ran inside GEMM2
