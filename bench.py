@@ -6,7 +6,8 @@ batch of seeded synthetic inputs already resident in HBM.  The headline
 workload is W4A16 decode (M=8 tokens, hidden 6144, inter 2048, 256 experts
 of which 32 are local, top_k 8), HBM-bound on weight bytes; the W4A16
 prefill workload (M=4096, biased router, SwiGLU limit 7), MFMA-bound, is
-reported alongside in the same line.  Weights, activations and routing are
+reported alongside in the same line, and so are the W4A4 (M=512) and
+MXFP8 x MXFP4 (M=65536) parity configurations.  Weights, activations and routing are
 rotated over several resident copies so that no step finds the previous
 steps' weights in the 256 MB MALL.
 
@@ -27,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
 METRIC = "fused-MoE fwd tokens/s + % HBM roofline (M=8) / % MFMA peak (M=4096)"
 
 
@@ -37,7 +39,10 @@ def log(*a):
 # ------------------------------------------------------------------ inputs
 class GpuInputs:
     """One workload's inputs on the GPU, prepared with the library's own
-    quantisers from the seeded bf16 draws, in `copies` resident copies."""
+    quantisers from the seeded bf16 draws, in `copies` resident copies.
+    W4A16: NVFP4 weights, bf16 x.  W4A4: NVFP4 weights and x (x's global
+    scale folded into w1_alpha); fc2_input_scale is 1 (not calibrated: these
+    inputs are for timing).  MXFP8_MXFP4: MXFP4 weights, MXFP8 x."""
 
     def __init__(self, wl, copies: int):
         import torch
@@ -45,37 +50,60 @@ class GpuInputs:
         import mixture_experts_forward_moe_amd as moe
         import synth
         self.wl = wl
-        E, H, I = wl.num_local_experts, wl.H, wl.I
+        E, H, I, M = wl.num_local_experts, wl.H, wl.I, wl.M
         raw = synth.make_raw(wl)
         self.topk_ids_np = raw.topk_ids
         dev = "cuda"
-        x = torch.from_numpy(raw.x.view(np.int16)).to(dev)
+        xb = torch.from_numpy(raw.x.view(np.int16)).to(dev)
         w1b = torch.from_numpy(raw.w1.view(np.int16)).to(dev)
         w2b = torch.from_numpy(raw.w2.view(np.int16)).to(dev)
         del raw
-        self.w1 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
-        self.w1_sf = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=dev)
-        self.w2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
-        self.w2_sf = torch.empty((E, H, I // 16), dtype=torch.uint8, device=dev)
-        self.w1_alpha = torch.empty(E, dtype=torch.float32, device=dev)
-        self.w2_alpha = torch.empty(E, dtype=torch.float32, device=dev)
-        moe.moe_nvfp4_global_scale(w1b, E, self.w1_alpha)
-        moe.moe_quantize_nvfp4(w1b, E, 2 * I, H, self.w1_alpha, self.w1, self.w1_sf)
-        moe.moe_nvfp4_global_scale(w2b, E, self.w2_alpha)
-        moe.moe_quantize_nvfp4(w2b, E, H, I, self.w2_alpha, self.w2, self.w2_sf)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.x_sf = None
+        self.fc2 = None
+        if wl.mode == moe.MXFP8_MXFP4:
+            self.w1 = torch.empty((E, 2 * I, H // 2), **u8)
+            self.w1_sf = torch.empty((E, 2 * I, H // 32), **u8)
+            self.w2 = torch.empty((E, H, I // 2), **u8)
+            self.w2_sf = torch.empty((E, H, I // 32), **u8)
+            moe.moe_quantize_mx(w1b, E * 2 * I, H, 1, self.w1, self.w1_sf)
+            moe.moe_quantize_mx(w2b, E * H, I, 1, self.w2, self.w2_sf)
+            self.w1_alpha = torch.ones(E, dtype=torch.float32, device=dev)
+            self.w2_alpha = torch.ones(E, dtype=torch.float32, device=dev)
+            self.x = torch.empty((M, H), **u8)
+            self.x_sf = torch.empty((M, H // 32), **u8)
+            moe.moe_quantize_mx(xb, M, H, 0, self.x, self.x_sf)
+        else:
+            self.w1 = torch.empty((E, 2 * I, H // 2), **u8)
+            self.w1_sf = torch.empty((E, 2 * I, H // 16), **u8)
+            self.w2 = torch.empty((E, H, I // 2), **u8)
+            self.w2_sf = torch.empty((E, H, I // 16), **u8)
+            self.w1_alpha = torch.empty(E, dtype=torch.float32, device=dev)
+            self.w2_alpha = torch.empty(E, dtype=torch.float32, device=dev)
+            moe.moe_nvfp4_global_scale(w1b, E, self.w1_alpha)
+            moe.moe_quantize_nvfp4(w1b, E, 2 * I, H, self.w1_alpha, self.w1, self.w1_sf)
+            moe.moe_nvfp4_global_scale(w2b, E, self.w2_alpha)
+            moe.moe_quantize_nvfp4(w2b, E, H, I, self.w2_alpha, self.w2, self.w2_sf)
+            if wl.mode == moe.W4A4:
+                xg = torch.empty(1, dtype=torch.float32, device=dev)
+                moe.moe_nvfp4_global_scale(xb, 1, xg)
+                self.x = torch.empty((M, H // 2), **u8)
+                self.x_sf = torch.empty((M, H // 16), **u8)
+                moe.moe_quantize_nvfp4(xb, 1, M, H, xg, self.x, self.x_sf)
+                self.w1_alpha *= xg
+                self.fc2 = torch.ones(1, dtype=torch.float32, device=dev)
+            else:
+                self.x = xb
         torch.cuda.synchronize()
         del w1b, w2b
-        assert wl.mode == moe.W4A16, "the benchmark workloads are W4A16"
-        self.x = x
         self.ids = torch.from_numpy(self.topk_ids_np).to(dev)
-        self.w = None
         _, wts = synth.make_routing(wl)
         self.w = torch.from_numpy(wts).to(dev)
         # resident copies, rotated step by step
         self.copies = [(self.x, self.ids, self.w, self.w1, self.w1_sf, self.w1_alpha, self.w2, self.w2_sf,
-                        self.w2_alpha)]
+                        self.w2_alpha, self.x_sf)]
         for _ in range(copies - 1):
-            self.copies.append(tuple(t.clone() for t in self.copies[0]))
+            self.copies.append(tuple(t.clone() if t is not None else None for t in self.copies[0]))
         torch.cuda.synchronize()
 
     def local_stats(self):
@@ -87,9 +115,9 @@ class GpuInputs:
         return routes, active
 
 
-def _opts(moe, wl, ws, tile, **kw):
+def _opts(moe, wl, ws, tile, fc2=None, **kw):
     return moe.make_opts(workspace=ws, tile=tile, swiglu_alpha=wl.swiglu_alpha, swiglu_beta=wl.swiglu_beta,
-                         swiglu_limit=wl.swiglu_limit, **kw)
+                         swiglu_limit=wl.swiglu_limit, fc2_input_scale=fc2, **kw)
 
 
 def time_graph(wl, steps: int, warmup: int, copies: int):
@@ -104,11 +132,11 @@ def time_graph(wl, steps: int, warmup: int, copies: int):
     tile = moe.default_tile(wl.M, wl.top_k, E, wl.mode)
     ws = torch.zeros(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.M, H), dtype=torch.int16, device="cuda")
-    opts = _opts(moe, wl, ws, tile)
+    opts = _opts(moe, wl, ws, tile, fc2=g.fc2)
 
     def step(i):
-        x, ids, w, w1, w1s, w1a, w2, w2s, w2a = g.copies[i % len(g.copies)]
-        moe.moe_forward(x, None, ids, w, w1, w1s, w1a, w2, w2s, w2a, wl.num_experts, wl.top_k, E,
+        x, ids, w, w1, w1s, w1a, w2, w2s, w2a, xs = g.copies[i % len(g.copies)]
+        moe.moe_forward(x, xs, ids, w, w1, w1s, w1a, w2, w2s, w2a, wl.num_experts, wl.top_k, E,
                         wl.local_expert_offset, wl.mode, out, H, I, opts=opts)
 
     for i in range(max(warmup, copies)):  # eager warm-up (also caches the launch shape)
@@ -157,12 +185,12 @@ def time_phases(wl, steps: int, warmup: int, copies: int):
         for e in row:
             e.record()
     torch.cuda.synchronize()
-    opts = _opts(moe, wl, ws, tile)
-    opts_ev = [_opts(moe, wl, ws, tile, phase_events=events[i]) for i in range(steps)]
+    opts = _opts(moe, wl, ws, tile, fc2=g.fc2)
+    opts_ev = [_opts(moe, wl, ws, tile, fc2=g.fc2, phase_events=events[i]) for i in range(steps)]
 
     def step(i, o):
-        x, ids, w, w1, w1s, w1a, w2, w2s, w2a = g.copies[i % len(g.copies)]
-        moe.moe_forward(x, None, ids, w, w1, w1s, w1a, w2, w2s, w2a, wl.num_experts, wl.top_k, E,
+        x, ids, w, w1, w1s, w1a, w2, w2s, w2a, xs = g.copies[i % len(g.copies)]
+        moe.moe_forward(x, xs, ids, w, w1, w1s, w1a, w2, w2s, w2a, wl.num_experts, wl.top_k, E,
                         wl.local_expert_offset, wl.mode, out, H, I, opts=o)
 
     for i in range(warmup):
@@ -204,6 +232,15 @@ def w4a16_bytes(wl, routes, active):
         weights=active * (w1 + w2),
         w1_per_expert=w1, w2_per_expert=w2,
     )
+
+
+def weight_bytes(wl, active):
+    """Codes and block scales of the active experts' W1 and W2 (NVFP4:
+    E4M3 per 16 elements; MXFP4: E8M0 per 32)."""
+    import synth
+    blk = 32 if wl.mode == synth.MXFP8_MXFP4 else 16
+    per = 3 * wl.H * wl.I // 2 + 3 * wl.H * wl.I // blk
+    return active * per
 
 
 def flops(wl, routes):
@@ -360,6 +397,24 @@ def main():
                            "tflops": tf2, "mfma_frac": tf2 / BF16_PEAK_TFLOPS, "gemm1_tflops": g1f,
                            "gemm1_mfma_frac": g1f / BF16_PEAK_TFLOPS, "phase_ms": r2["phase_ms"],
                            "peak_tflops": BF16_PEAK_TFLOPS}
+    if not args.no_secondary:
+        # the other two quantisation modes, on their parity configurations
+        for name, key, peak, steps3, note in (
+                ("w4a4", "w4a4_nvfp4", BF16_PEAK_TFLOPS, 10, "NVFP4 x and weights, bf16 MFMA after decode"),
+                ("mx", "mxfp8_mxfp4_large", FP8_PEAK_TFLOPS, 4,
+                 "MXFP8 x, MXFP4 weights, scaled fp8 x fp4 MFMA (peak: dense fp8)")):
+            wl3 = synth.WORKLOADS[key]
+            log(f"bench: {wl3.name}: {steps3} steps (eager, per-kernel events)")
+            r3 = time_phases(wl3, steps3, 2, 1)
+            fl3 = flops(wl3, r3["local_routes"])
+            tf3 = fl3 / (r3["ms_per_step"] * 1e-3) / 1e12
+            wb = weight_bytes(wl3, r3["active_experts"])
+            line[name] = {"workload": wl3.name, "M": wl3.M, "H": wl3.H, "I": wl3.I,
+                          "local_experts": wl3.num_local_experts, "tokens_per_s": wl3.M * steps3 / r3["seconds"],
+                          "ms_per_step": r3["ms_per_step"], "tile": r3["tile"], "local_routes": r3["local_routes"],
+                          "tflops": tf3, "mfma_frac": tf3 / peak, "peak_tflops": peak, "phase_ms": r3["phase_ms"],
+                          "weight_bytes": wb, "weights_hbm_frac": wb / (r3["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "note": note}
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(wl)
