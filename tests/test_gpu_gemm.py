@@ -236,6 +236,31 @@ def test_decode_path_workspace_reuse():
     assert np.all(counters == 0), np.nonzero(counters)
 
 
+def test_decode_sized_batch_with_unaligned_scales():
+    """The decode kernels read scale pairs as aligned 32-bit words; scale
+    arrays at a 2-byte offset must take the tiled path instead and give the
+    same results as aligned ones (deterministic finalize either way)."""
+    import torch
+
+    from gpu_util import DeviceProblem, check_close, host, say
+    say("decode-sized batch, scale arrays at a 2-byte offset")
+    p = decode_case("offset_swiglu")
+    d = DeviceProblem(p)
+    want = oracle.forward_tokens(p, np.arange(p.M))
+    aligned = d.forward(tile=16)
+    for name in ("w1_sf", "w2_sf"):
+        t = getattr(d, name)
+        base = torch.empty(t.numel() + 2, dtype=torch.uint8, device="cuda")
+        view = base[2:].view(t.shape)
+        view.copy_(t)
+        assert view.data_ptr() % 4 == 2
+        setattr(d, name, view)
+    shifted = d.forward(tile=16)
+    torch.cuda.synchronize()
+    check_close(host(shifted, np.uint16), want, p.mode, "unaligned scales")
+    check_close(host(aligned, np.uint16), want, p.mode, "aligned scales")
+
+
 def test_decode_path_graph_replay():
     """The single-launch decode path captured in a HIP graph: every replay,
     with eager calls on the same workspace in between, gives the eager
