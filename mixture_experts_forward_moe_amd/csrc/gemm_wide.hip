@@ -44,6 +44,7 @@
 //    are read by one XCD and the load is the same on all eight.
 #include "device_common.h"
 #include "internal.h"
+#include "tile_order.h"
 
 namespace moe {
 
@@ -353,36 +354,7 @@ __global__ __launch_bounds__(WT, 2) void wide_gemm_kernel(const WArgs a) {
   }
   if (r >= T) return;
 
-  // tile of rank r: count the tiles of each height (1..8 row groups of 16),
-  // then find the one that holds rank r, tiles of one height in plan order
-  __shared__ int cls_n[9];
-  __shared__ int wave_n[4];
-  __shared__ int found;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto height = [&](int pt) -> int { return (min(WM, a.tile_limit[pt] - pt * WM) + 15) >> 4; };
-  if (tid < 9) cls_n[tid] = 0;
-  __syncthreads();
-  for (int pt = tid; pt < T; pt += WT) atomicAdd(&cls_n[height(pt)], 1);
-  __syncthreads();
-  int c = 8, before = 0;
-  while (before + cls_n[c] <= r) before += cls_n[c--];
-  const int k = r - before;  // index among the tiles of height c
-  int seen = 0;
-  for (int base = 0; base < T; base += WT) {
-    const int pt = base + tid;
-    const bool hit = pt < T && height(pt) == c;
-    const unsigned long long bal = __ballot(hit);
-    if (lane == 0) wave_n[wave] = __popcll(bal);
-    __syncthreads();
-    int off = seen;
-    for (int w = 0; w < wave; w++) off += wave_n[w];
-    const int idx = off + __popcll(bal & ((1ull << lane) - 1));
-    if (hit && idx == k) found = pt;
-    seen += wave_n[0] + wave_n[1] + wave_n[2] + wave_n[3];
-    __syncthreads();
-    if (seen > k) break;
-  }
-  const int pt = __builtin_amdgcn_readfirstlane(found);
+  const int pt = tile_of_rank(a.tile_limit, T, WM, r, WT);
   const int e = __builtin_amdgcn_readfirstlane(a.tile_expert[pt]);
   const int slot0 = pt * WM;
   const int valid = __builtin_amdgcn_readfirstlane(min(WM, a.tile_limit[pt] - slot0));

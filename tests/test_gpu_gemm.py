@@ -26,6 +26,8 @@ CASES = {
     "w4a4_tall": (oracle.W4A4, dict(M=450, H=256, I=384, E=6, El=6, k=3, seed=53, router_bias_std=0.7)),
     "mx_basic": (oracle.MXFP8_MXFP4, dict(M=40, H=256, I=256, E=8, El=8, k=2, seed=46)),
     "mx_offset": (oracle.MXFP8_MXFP4, dict(M=45, H=512, I=256, E=16, El=6, k=4, seed=47, offset=9)),
+    "mx_tall": (oracle.MXFP8_MXFP4, dict(M=450, H=512, I=512, E=8, El=6, k=3, seed=54, offset=1,
+                                         router_bias_std=0.7, swiglu_limit=2.0)),
 }
 
 _cache = {}
@@ -111,7 +113,7 @@ def test_forward(name, tile):
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("name", ["w4a16_basic", "w4a16_stream_offset", "w4a4_offset", "mx_offset"])
+@pytest.mark.parametrize("name", ["w4a16_basic", "w4a16_stream_offset", "w4a4_offset", "mx_offset", "mx_tall"])
 def test_atomic_finalize_and_accumulate(name):
     import torch
 
