@@ -19,6 +19,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 W4A16, W4A4, MXFP8_MXFP4 = 0, 1, 2
 ELEM_E4M3, ELEM_E2M1 = 0, 1
+ACT_SWIGLU, ACT_GEGLU_TANH = 0, 1   # FC1 activations (SiTU is SwiGLU with situ_beta > 0)
 
 
 def build(force: bool = True) -> str:
@@ -44,6 +45,7 @@ class _Moe(ctypes.Structure):
         ("w2", ctypes.c_void_p), ("w2_sf", ctypes.c_void_p), ("w2_alpha", ctypes.c_void_p),
         ("swiglu_alpha", ctypes.c_float), ("swiglu_beta", ctypes.c_float), ("swiglu_limit", ctypes.c_float),
         ("fc2_input_scale", ctypes.c_float), ("routed_scaling_factor", ctypes.c_float),
+        ("activation", ctypes.c_int), ("situ_beta", ctypes.c_float), ("situ_linear_beta", ctypes.c_float),
     ]
 
 
@@ -71,6 +73,8 @@ def lib():
             "orc_route_slots": ([I64, I, I, I], I64),
             "orc_sort": ([P, I64, I, I, I, I, P, P, P, P, P, P, P], None),
             "orc_swiglu": ([F, F, F, F, F], D),
+            "orc_geglu_tanh": ([F, F], D),
+            "orc_situ": ([F, F, F, F], D),
             "orc_gemm1_route": ([P, I64, I, P, P, P, P], None),
             "orc_gemm2_route": ([P, I, P, P], None),
             "orc_finalize": ([P, P, P, I64, I, I, F, I, P, P], None),
@@ -130,6 +134,17 @@ def e2m1_encode(v: np.ndarray) -> np.ndarray:
 
 def swiglu(g: float, u: float, alpha=1.0, beta=0.0, limit=float(np.finfo(np.float32).max)) -> float:
     return lib().orc_swiglu(g, u, alpha, beta, limit)
+
+
+def geglu_tanh(g: float, u: float) -> float:
+    """gelu_tanh(g) * u in fp64 (activation_type GegluTanh)"""
+    return lib().orc_geglu_tanh(g, u)
+
+
+def situ(g: float, u: float, beta: float, linear_beta: float = 0.0) -> float:
+    """SiTU gate beta * tanh(g / beta) * sigmoid(g) times the up branch,
+    clamped by linear_beta * tanh(u / linear_beta) when linear_beta > 0"""
+    return lib().orc_situ(g, u, beta, linear_beta)
 
 
 # ---------------------------------------------------------------- quantisers
@@ -246,6 +261,9 @@ class Problem:
     fc2_input_scale: float = 0.0
     routed_scaling_factor: float = 1.0
     x_row_stride: int = 0        # 0: contiguous
+    activation: int = 0          # ACT_SWIGLU (SiTU when situ_beta > 0) | ACT_GEGLU_TANH
+    situ_beta: float = 0.0
+    situ_linear_beta: float = 0.0
 
     def struct(self) -> _Moe:
         s = _Moe()
@@ -261,6 +279,7 @@ class Problem:
         s.x_row_stride = stride
         s.swiglu_alpha, s.swiglu_beta, s.swiglu_limit = self.swiglu_alpha, self.swiglu_beta, self.swiglu_limit
         s.fc2_input_scale, s.routed_scaling_factor = self.fc2_input_scale, self.routed_scaling_factor
+        s.activation, s.situ_beta, s.situ_linear_beta = self.activation, self.situ_beta, self.situ_linear_beta
         self._keep = s
         return s
 
@@ -381,7 +400,8 @@ def quantize_problem(raw, calibrate: bool = True) -> Problem:
         x, x_sf = mx_quantize_bf16(raw.x, ELEM_E4M3)
     p = Problem(wl.mode, wl.M, H, I, wl.top_k, wl.num_experts, E, wl.local_expert_offset,
                 np.ascontiguousarray(x), x_sf, raw.topk_ids, raw.topk_weights, w1, w1_sf, a1, w2, w2_sf, a2,
-                swiglu_alpha=wl.swiglu_alpha, swiglu_beta=wl.swiglu_beta, swiglu_limit=wl.swiglu_limit)
+                swiglu_alpha=wl.swiglu_alpha, swiglu_beta=wl.swiglu_beta, swiglu_limit=wl.swiglu_limit,
+                activation=wl.activation, situ_beta=wl.situ_beta, situ_linear_beta=wl.situ_linear_beta)
     if wl.mode == W4A4:
         p.extra_w2_alpha_raw = a2.copy()
         if calibrate:

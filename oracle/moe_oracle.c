@@ -11,9 +11,10 @@
  *  - "flashinfer.fused_moe.cute_dsl_fused_moe" (FlashInfer API reference),
  *    Parameters x / x_sf / w1_alpha / w2_alpha / fc2_input_scale /
  *    num_local_experts / local_expert_offset / use_fused_finalize /
- *    swiglu_alpha, swiglu_beta, swiglu_limit and the signature's defaults:
- *    the three quantisation modes, the per-expert fp32 scales, the local
- *    expert share and the SwiGLU parameters.
+ *    swiglu_alpha, swiglu_beta, swiglu_limit, activation_type, situ_beta,
+ *    situ_linear_beta and the signature's defaults: the three quantisation
+ *    modes, the per-expert fp32 scales, the local expert share, the SwiGLU
+ *    parameters and the gated GeGLU-tanh / SiTU activations.
  *  - "flashinfer.fused_moe.alphamoe_nvfp4_routed_moe", summary and
  *    Parameters: packed E2M1 with linear E4M3 block-16 scales, route-order
  *    finalize seeded from the existing output, `accumulate`,
@@ -49,6 +50,7 @@
 
 enum { ORC_W4A16 = 0, ORC_W4A4 = 1, ORC_MXFP8_MXFP4 = 2 };
 enum { ORC_ELEM_E4M3 = 0, ORC_ELEM_E2M1 = 1 };
+enum { ORC_ACT_SWIGLU = 0, ORC_ACT_GEGLU_TANH = 1 };
 
 /* ------------------------------------------------------------------------ */
 /* Number formats (OCP MX v1.0 / OCP FP8, as named by the pages)            */
@@ -368,6 +370,9 @@ typedef struct {
   float swiglu_alpha, swiglu_beta, swiglu_limit;
   float fc2_input_scale; /* W4A4: global scale of the FC1-output requantisation */
   float routed_scaling_factor;
+  int activation;         /* ORC_ACT_SWIGLU (SwiGLU, or SiTU when situ_beta > 0) | ORC_ACT_GEGLU_TANH */
+  float situ_beta;        /* > 0 selects SiTU; 0 = unset */
+  float situ_linear_beta; /* > 0: SiTU tanh clamp of the up branch; 0 = unset */
 } orc_moe_t;
 
 static int sf_block(int mode) { return mode == ORC_MXFP8_MXFP4 ? 32 : 16; }
@@ -438,6 +443,36 @@ double orc_swiglu(float g, float u, float alpha, float beta, float limit) {
   return gc * sig * (uc + (double)beta);
 }
 
+/* GeGLU with the tanh approximation of GELU ("flashinfer.fused_moe.
+ * cute_dsl_fused_moe", Parameters, activation_type GegluTanh):
+ * y = gelu_tanh(g) * u, gelu_tanh(x) = x/2 * (1 + tanh(sqrt(2/pi) *
+ * (x + 0.044715 x^3))), the published tanh form of GELU (Hendrycks and
+ * Gimpel).  Evaluated in fp64. */
+double orc_geglu_tanh(float g, float u) {
+  double x = g;
+  double z = sqrt(2.0 / 3.14159265358979323846) * (x + 0.044715 * x * x * x);
+  return 0.5 * x * (1.0 + tanh(z)) * (double)u;
+}
+
+/* SiTU (same Parameters, situ_beta and situ_linear_beta): the gate
+ * beta * tanh(g / beta) * sigmoid(g) in place of SiLU's g * sigmoid(g), and
+ * when linear_beta > 0 the up branch clamped the same way,
+ * linear_beta * tanh(u / linear_beta).  Evaluated in fp64. */
+double orc_situ(float g, float u, float beta, float linear_beta) {
+  double b = beta;
+  double gate = b * tanh((double)g / b) / (1.0 + exp(-(double)g));
+  double up = u;
+  if (linear_beta > 0.0f) up = (double)linear_beta * tanh((double)u / (double)linear_beta);
+  return gate * up;
+}
+
+/* The FC1 activation of one gate/up pair, as the problem selects it. */
+static double gated_act(const orc_moe_t* p, float g, float u) {
+  if (p->activation == ORC_ACT_GEGLU_TANH) return orc_geglu_tanh(g, u);
+  if (p->situ_beta > 0.0f) return orc_situ(g, u, p->situ_beta, p->situ_linear_beta);
+  return orc_swiglu(g, u, p->swiglu_alpha, p->swiglu_beta, p->swiglu_limit);
+}
+
 /* fp32 accumulator value times the per-expert fp32 scale, in fp32. */
 static float scale_acc(double acc, float alpha) {
   float a = (float)acc;
@@ -456,7 +491,7 @@ static void swiglu_row_and_requant(const orc_moe_t* p, int le, const double* G, 
   for (int j = 0; j < I; j++) {
     float g = scale_acc(G[j], p->w1_alpha[le]);
     float u = scale_acc(U[j], p->w1_alpha[le]);
-    uint16_t b = orc_bf16_round(orc_swiglu(g, u, p->swiglu_alpha, p->swiglu_beta, p->swiglu_limit));
+    uint16_t b = orc_bf16_round(gated_act(p, g, u));
     if (y1_bf16) y1_bf16[j] = b;
     y[j] = orc_bf16_value(b);
   }
@@ -692,7 +727,7 @@ float orc_fc2_input_scale(const orc_moe_t* p) {
         for (int n = 0; n < I; n++) {
           float g = scale_acc(dot(a, wd1 + (int64_t)n * H, H), p->w1_alpha[le]);
           float u = scale_acc(dot(a, wd1 + (int64_t)(I + n) * H, H), p->w1_alpha[le]);
-          uint16_t b = orc_bf16_round(orc_swiglu(g, u, p->swiglu_alpha, p->swiglu_beta, p->swiglu_limit));
+          uint16_t b = orc_bf16_round(gated_act(p, g, u));
           float v = fabsf(orc_bf16_value(b));
           if (v > local) local = v;
         }

@@ -124,6 +124,9 @@ class Workload:
     swiglu_alpha: float = 1.0
     swiglu_beta: float = 0.0
     swiglu_limit: float = float(np.finfo(np.float32).max)
+    activation: int = 0               # 0 SwiGLU (SiTU when situ_beta > 0), 1 GeGLU-tanh
+    situ_beta: float = 0.0
+    situ_linear_beta: float = 0.0
     x_std: float = 1.0
     w_std: float = 0.02
     sample_tokens: int = 0            # >0: parity on this many sampled tokens

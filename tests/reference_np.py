@@ -112,6 +112,25 @@ def swiglu(g, u, alpha, beta, limit):
     return (gc * torch.sigmoid(float(alpha) * gc) * (uc + float(beta))).numpy()
 
 
+def gated_act(p, g, u):
+    """FC1 activation of an oracle.Problem-like p, from torch's own routines
+    (gelu with the tanh approximation, tanh, sigmoid) in fp64"""
+    if getattr(p, "activation", 0) == 1:
+        gt = torch.from_numpy(np.asarray(g, np.float64))
+        ut = torch.from_numpy(np.asarray(u, np.float64))
+        return (torch.nn.functional.gelu(gt, approximate="tanh") * ut).numpy()
+    if getattr(p, "situ_beta", 0.0) > 0.0:
+        gt = torch.from_numpy(np.asarray(g, np.float64))
+        ut = torch.from_numpy(np.asarray(u, np.float64))
+        b = float(np.float32(p.situ_beta))
+        up = ut
+        if p.situ_linear_beta > 0.0:
+            lb = float(np.float32(p.situ_linear_beta))
+            up = lb * torch.tanh(ut / lb)
+        return (b * torch.tanh(gt / b) * torch.sigmoid(gt) * up).numpy()
+    return swiglu(g, u, p.swiglu_alpha, p.swiglu_beta, p.swiglu_limit)
+
+
 def forward_tokens(p, tokens):
     """out bf16 bits [len(tokens), H] for an oracle.Problem-like object p."""
     H, I, k = p.H, p.I, p.top_k
@@ -137,7 +156,7 @@ def forward_tokens(p, tokens):
             al1 = np.float32(p.w1_alpha[le])
             g = (gu[:I].astype(np.float32) * al1).astype(np.float32)
             u = (gu[I:].astype(np.float32) * al1).astype(np.float32)
-            y1 = bf16_vals(to_bf16_bits(swiglu(g, u, p.swiglu_alpha, p.swiglu_beta, p.swiglu_limit)))
+            y1 = bf16_vals(to_bf16_bits(gated_act(p, g, u)))
             if p.mode == W4A16:
                 a2 = y1
             elif p.mode == W4A4:

@@ -36,6 +36,12 @@ SMALL = [
     (oracle.W4A4, dict(M=9, H=64, I=128, E=12, El=6, k=3, seed=24, offset=3)),
     (oracle.MXFP8_MXFP4, dict(M=12, H=128, I=64, E=8, El=8, k=2, seed=25)),
     (oracle.MXFP8_MXFP4, dict(M=9, H=96, I=128, E=12, El=4, k=3, seed=26, offset=8)),
+    # the other gated FC1 activations: GeGLU-tanh, SiTU (with and without the up-branch clamp)
+    (oracle.W4A16, dict(M=10, H=64, I=96, E=8, El=8, k=2, seed=27, activation=oracle.ACT_GEGLU_TANH)),
+    (oracle.W4A16, dict(M=10, H=64, I=64, E=8, El=6, k=3, seed=28, offset=1, situ_beta=0.1,
+                        situ_linear_beta=0.08)),
+    (oracle.W4A4, dict(M=9, H=64, I=64, E=8, El=8, k=2, seed=29, situ_beta=0.1)),
+    (oracle.MXFP8_MXFP4, dict(M=9, H=96, I=64, E=8, El=8, k=2, seed=30, activation=oracle.ACT_GEGLU_TANH)),
 ]
 
 
@@ -106,6 +112,42 @@ def test_swiglu_closed_forms():
     assert oracle.swiglu(-9.0, 1.0, 1.0, 0.0, lim) == pytest.approx(-9.0 / (1 + math.exp(9.0)), rel=1e-15)
     a32 = float(np.float32(1.702))   # the parameters are fp32
     assert oracle.swiglu(1.5, 2.0, 1.702, 1.0, lim) == pytest.approx(1.5 / (1 + math.exp(-a32 * 1.5)) * 3.0, rel=1e-15)
+
+
+def test_geglu_tanh_pins():
+    import torch
+    # closed forms: zero gate, saturation on both sides
+    assert oracle.geglu_tanh(0.0, 5.0) == 0.0
+    assert oracle.geglu_tanh(40.0, 3.0) == 120.0
+    assert abs(oracle.geglu_tanh(-40.0, 3.0)) < 1e-20
+    xs = [float(np.float32(v)) for v in np.linspace(-6.0, 6.0, 97)]
+    for x in xs:
+        # gelu(x) - gelu(-x) = x holds for the tanh form (tanh is odd)
+        assert oracle.geglu_tanh(x, 1.0) - oracle.geglu_tanh(-x, 1.0) == pytest.approx(x, rel=1e-14, abs=1e-15)
+        # torch's tanh-approximate GELU (library routine), fp64
+        want = float(torch.nn.functional.gelu(torch.tensor(x, dtype=torch.float64), approximate="tanh")) * 1.5
+        assert oracle.geglu_tanh(x, 1.5) == pytest.approx(want, rel=1e-14, abs=1e-300)
+        # and it stays within the approximation's error of the exact GELU x * Phi(x)
+        assert abs(oracle.geglu_tanh(x, 1.0) - x * 0.5 * (1.0 + math.erf(x / math.sqrt(2.0)))) < 1e-3
+
+
+def test_situ_pins():
+    xs = [float(np.float32(v)) for v in np.linspace(-8.0, 8.0, 65)]
+    for g in xs:
+        # beta -> infinity: beta * tanh(g / beta) -> g, so SiTU is SwiGLU (silu(g) * u)
+        assert oracle.situ(g, 1.25, 1e30) == pytest.approx(oracle.swiglu(g, 1.25), rel=1e-12, abs=1e-300)
+        # the gate is bounded by beta
+        assert abs(oracle.situ(g, 1.0, 0.5)) <= 0.5
+        # the up-branch clamp is odd in u and bounded by its beta
+        assert oracle.situ(g, -3.0, 0.5, 0.25) == -oracle.situ(g, 3.0, 0.5, 0.25)
+        assert abs(oracle.situ(g, 1e6, 0.5, 0.25)) <= 0.5 * 0.25 * (1 + 1e-15)
+    assert oracle.situ(0.0, 3.0, 0.5) == 0.0
+    b = float(np.float32(0.5))
+    # saturation: g >> beta gives beta * u, g << -beta gives ~0
+    assert oracle.situ(40.0, 3.0, 0.5) == pytest.approx(b * 3.0, rel=1e-15)
+    assert abs(oracle.situ(-40.0, 3.0, 0.5)) < 1e-16
+    # small |g| and |u|: tanh(z) ~ z, the gate is ~ silu(g) and the clamp ~ identity
+    assert oracle.situ(1e-4, 2e-4, 0.5, 0.25) == pytest.approx(oracle.swiglu(1e-4, 2e-4), rel=1e-6)
 
 
 def test_power_of_two_w2_alpha_scales_y2_exactly():
