@@ -117,7 +117,8 @@ class GpuInputs:
 
 def _opts(moe, wl, ws, tile, fc2=None, **kw):
     return moe.make_opts(workspace=ws, tile=tile, swiglu_alpha=wl.swiglu_alpha, swiglu_beta=wl.swiglu_beta,
-                         swiglu_limit=wl.swiglu_limit, fc2_input_scale=fc2, **kw)
+                         swiglu_limit=wl.swiglu_limit, activation=wl.activation, situ_beta=wl.situ_beta,
+                         situ_linear_beta=wl.situ_linear_beta, fc2_input_scale=fc2, **kw)
 
 
 def time_graph(wl, steps: int, warmup: int, copies: int):
@@ -415,6 +416,27 @@ def main():
                           "tflops": tf3, "mfma_frac": tf3 / peak, "peak_tflops": peak, "phase_ms": r3["phase_ms"],
                           "weight_bytes": wb, "weights_hbm_frac": wb / (r3["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "note": note}
+    if not args.no_secondary:
+        # the other gated FC1 activations on the decode and prefill workloads: the decode forward in
+        # graph replay (same roofline unit as the headline) and the prefill GEMM1 with per-kernel events
+        import dataclasses
+        acts = {}
+        for name, kw in (("geglu_tanh", dict(activation=1)), ("situ", dict(situ_beta=0.5, situ_linear_beta=1.0))):
+            wd = dataclasses.replace(wl, **kw)
+            log(f"bench: {wd.name} with {name}: {max(20, args.steps // 4)} steps (graph replay)")
+            rd = time_graph(wd, max(20, args.steps // 4), max(4, args.warmup // 4), args.copies)
+            fd = by["forward"] / (rd["gpu_ms_per_step"] * 1e-3) / 1e9
+            wp = dataclasses.replace(synth.WORKLOADS["w4a16_prefill"], swiglu_limit=float(np.finfo(np.float32).max),
+                                     **kw)
+            rp = time_phases(wp, 10, 3, args.copies)
+            g1 = 4.0 * wp.H * wp.I * rp["local_routes"] / (rp["phase_ms"]["gemm1"] * 1e-3) / 1e12
+            acts[name] = {"params": kw, "decode_ms_per_forward": rd["gpu_ms_per_step"], "decode_hbm_frac": fd / HBM_PEAK_GBS,
+                          "prefill_gemm1_ms": rp["phase_ms"]["gemm1"], "prefill_gemm1_mfma_frac": g1 / BF16_PEAK_TFLOPS}
+        acts["swiglu"] = {"decode_ms_per_forward": f_ms, "decode_hbm_frac": f_gbs / HBM_PEAK_GBS,
+                          "prefill_gemm1_ms": line["prefill"]["phase_ms"]["gemm1"],
+                          "prefill_gemm1_mfma_frac": line["prefill"]["gemm1_mfma_frac"],
+                          "note": "prefill with SwiGLU limit 7 (its workload); the others without a limit"}
+        line["activations"] = acts
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(wl)

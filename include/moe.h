@@ -166,6 +166,34 @@ moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, cons
                                       const float* fc2_input_scale, void* y1, uint8_t* y1_sf,
                                       moe_stream_t stream);
 
+/* FC1 activations ("flashinfer.fused_moe.cute_dsl_fused_moe", Parameters
+ * activation_type, situ_beta, situ_linear_beta). */
+typedef enum moe_activation {
+  MOE_ACT_SWIGLU = 0,      /* gated SwiGLU with swiglu_alpha / beta / limit; SiTU when situ_beta > 0 */
+  MOE_ACT_GEGLU_TANH = 1,  /* gated GeGLU, tanh-approximate GELU of the gate */
+  MOE_ACT_RELU2 = 2        /* non-gated ReLU^2: not implemented, MOE_ERR_UNSUPPORTED */
+} moe_activation_t;
+
+/* moe_grouped_gemm1_act: moe_grouped_gemm1_swiglu with the FC1 activation
+ * chosen by `activation` (same Parameters of cute_dsl_fused_moe):
+ *   MOE_ACT_SWIGLU, situ_beta == 0: the SwiGLU above.
+ *   MOE_ACT_SWIGLU, situ_beta  > 0: SiTU,
+ *       y1 = situ_beta * tanh(g / situ_beta) * sigmoid(g) * u',
+ *       u' = situ_linear_beta * tanh(u / situ_linear_beta) if situ_linear_beta > 0, else u.
+ *   MOE_ACT_GEGLU_TANH: y1 = g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3))) * u.
+ * Everything else (inputs, layouts, requantisation, rounding once to bf16)
+ * is as in moe_grouped_gemm1_swiglu.  MOE_ERR_INVALID_ARGUMENT: an unknown
+ * activation; situ_beta or situ_linear_beta negative or not finite;
+ * situ_linear_beta > 0 without situ_beta > 0; GeGLU or SiTU together with
+ * non-default SwiGLU parameters (1, 0, FLT_MAX) or GeGLU with SiTU
+ * parameters.  MOE_ERR_UNSUPPORTED: MOE_ACT_RELU2. */
+moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const uint8_t* x_sf,
+                                   int64_t x_row_stride, const moe_plan_t* plan, const uint8_t* w1,
+                                   const uint8_t* w1_sf, const float* w1_alpha, int H, int I,
+                                   int activation, float swiglu_alpha, float swiglu_beta, float swiglu_limit,
+                                   float situ_beta, float situ_linear_beta, const float* fc2_input_scale,
+                                   void* y1, uint8_t* y1_sf, moe_stream_t stream);
+
 /* moe_grouped_gemm2: for every valid slot s of local expert e, multiply the
  * stored FC1 output (decoded as moe_grouped_gemm1_swiglu wrote it; in W4A4
  * fc2_input_scale is part of w2_alpha) by W2[e]^T in fp32 and scale by
@@ -216,6 +244,10 @@ typedef struct moe_opts {
   void** phase_events;           /* optional: MOE_NUM_PHASE_EVENTS hipEvent_t recorded on the
                                     stream before sort, after sort, after GEMM1, after GEMM2,
                                     after finalize (timing); NULL = none */
+  int activation;                /* moe_activation_t, default MOE_ACT_SWIGLU (rules as in
+                                    moe_grouped_gemm1_act) */
+  float situ_beta;               /* default 0 (SwiGLU); > 0 selects SiTU */
+  float situ_linear_beta;        /* default 0 (no up-branch clamp) */
 } moe_opts_t;
 
 #define MOE_NUM_PHASE_EVENTS 5

@@ -3,6 +3,7 @@
 // check runs before anything is enqueued; nothing here allocates device
 // memory or synchronises the host.
 #include <float.h>
+#include <cmath>
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -64,6 +65,29 @@ moe_status_t shape_check(int H, int I, int mode) {
   if (H <= 0 || I <= 0) return MOE_ERR_INVALID_ARGUMENT;
   const int q = (mode == MOE_QUANT_MXFP8_MXFP4) ? 256 : 128;
   if (H % q != 0 || I % q != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// The FC1 activation's kernel arguments from the ABI's parameters (rules in
+// moe.h, moe_grouped_gemm1_act).
+moe_status_t make_act(int activation, float alpha, float beta, float limit, float situ_beta, float situ_lin,
+                      GateAct* out) {
+  if (activation == MOE_ACT_RELU2) return MOE_ERR_UNSUPPORTED;
+  if (activation != MOE_ACT_SWIGLU && activation != MOE_ACT_GEGLU_TANH) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(limit > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(situ_beta >= 0.0f) || !std::isfinite(situ_beta)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(situ_lin >= 0.0f) || !std::isfinite(situ_lin)) return MOE_ERR_INVALID_ARGUMENT;
+  if (situ_lin > 0.0f && !(situ_beta > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
+  const bool swiglu_default = alpha == 1.0f && beta == 0.0f && limit == FLT_MAX;
+  GateAct a = {ACT_SWIGLU, alpha, beta, limit, situ_beta, situ_lin};
+  if (activation == MOE_ACT_GEGLU_TANH) {
+    if (!swiglu_default || situ_beta > 0.0f) return MOE_ERR_INVALID_ARGUMENT;
+    a.kind = ACT_GEGLU_TANH;
+  } else if (situ_beta > 0.0f) {
+    if (!swiglu_default) return MOE_ERR_INVALID_ARGUMENT;
+    a.kind = ACT_SITU;
+  }
+  *out = a;
   return MOE_OK;
 }
 
@@ -148,12 +172,12 @@ moe_status_t moe_sort(const int32_t* topk_ids, int M, int top_k, int num_experts
   return dev(launch_sort(topk_ids, M, top_k, local_expert_offset, route_order, plan, (hipStream_t)stream));
 }
 
-moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, const uint8_t* x_sf,
-                                      int64_t x_row_stride, const moe_plan_t* plan, const uint8_t* w1,
-                                      const uint8_t* w1_sf, const float* w1_alpha, int H, int I,
-                                      float swiglu_alpha, float swiglu_beta, float swiglu_limit,
-                                      const float* fc2_input_scale, void* y1, uint8_t* y1_sf,
-                                      moe_stream_t stream) {
+moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const uint8_t* x_sf,
+                                   int64_t x_row_stride, const moe_plan_t* plan, const uint8_t* w1,
+                                   const uint8_t* w1_sf, const float* w1_alpha, int H, int I,
+                                   int activation, float swiglu_alpha, float swiglu_beta, float swiglu_limit,
+                                   float situ_beta, float situ_linear_beta, const float* fc2_input_scale,
+                                   void* y1, uint8_t* y1_sf, moe_stream_t stream) {
   if (!mode_ok(mode) || !plan_ok(plan)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status_t s = shape_check(H, I, mode);
   if (s != MOE_OK) return s;
@@ -166,8 +190,9 @@ moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, cons
   if (x_row_stride != 0 && x_row_stride < row_units) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t stride = x_row_stride ? x_row_stride : row_units;
   if ((stride * (mode == MOE_QUANT_W4A16 ? 2 : 1)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
-  if (!(swiglu_limit > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
   Gemm1Params p;
+  s = make_act(activation, swiglu_alpha, swiglu_beta, swiglu_limit, situ_beta, situ_linear_beta, &p.act);
+  if (s != MOE_OK) return s;
   p.mode = mode;
   p.x = x;
   p.x_sf = x_sf;
@@ -178,14 +203,22 @@ moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, cons
   p.w1_alpha = w1_alpha;
   p.H = H;
   p.I = I;
-  p.swiglu_alpha = swiglu_alpha;
-  p.swiglu_beta = swiglu_beta;
-  p.swiglu_limit = swiglu_limit;
   p.fc2_input_scale = fc2_input_scale;
   p.y1 = y1;
   p.y1_sf = y1_sf;
   if (plan->M == 0) return MOE_OK;
   return dev(launch_gemm1(p, (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, const uint8_t* x_sf,
+                                      int64_t x_row_stride, const moe_plan_t* plan, const uint8_t* w1,
+                                      const uint8_t* w1_sf, const float* w1_alpha, int H, int I,
+                                      float swiglu_alpha, float swiglu_beta, float swiglu_limit,
+                                      const float* fc2_input_scale, void* y1, uint8_t* y1_sf,
+                                      moe_stream_t stream) {
+  return moe_grouped_gemm1_act(mode, x, x_sf, x_row_stride, plan, w1, w1_sf, w1_alpha, H, I, MOE_ACT_SWIGLU,
+                               swiglu_alpha, swiglu_beta, swiglu_limit, 0.0f, 0.0f, fc2_input_scale, y1, y1_sf,
+                               stream);
 }
 
 moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint8_t* y1_sf,
@@ -296,6 +329,10 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   if ((quant_mode == MOE_QUANT_W4A16) != (x_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
   if ((quant_mode == MOE_QUANT_W4A4) != (opts->fc2_input_scale != NULL)) return MOE_ERR_INVALID_ARGUMENT;
   if (num_local_experts > MAX_LOCAL_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  GateAct act;
+  s = make_act(opts->activation, opts->swiglu_alpha, opts->swiglu_beta, opts->swiglu_limit, opts->situ_beta,
+               opts->situ_linear_beta, &act);
+  if (s != MOE_OK) return s;
   const int tile = opts->tile ? opts->tile : moe_default_tile(M, top_k, num_local_experts, quant_mode);
   if (!pow2_in(tile, 16, 256)) return MOE_ERR_UNSUPPORTED;
   const size_t need = moe_workspace_size(M, H, I, top_k, num_local_experts, tile, quant_mode, opts->finalize_mode);
@@ -343,9 +380,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
     d.w2_alpha = w2_alpha;
     d.H = H;
     d.I = I;
-    d.swiglu_alpha = opts->swiglu_alpha;
-    d.swiglu_beta = opts->swiglu_beta;
-    d.swiglu_limit = opts->swiglu_limit;
+    d.act = act;
     d.y1 = (uint16_t*)y1;
     d.y2 = y2;
     d.counters = counters;
@@ -371,9 +406,10 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   if (!fused && opts->finalize_mode == MOE_FINALIZE_ATOMIC && !opts->accumulate) {
     if (launch_zero_fill(out, (size_t)M * H * 2, st) != hipSuccess) return MOE_ERR_DEVICE;
   }
-  s = moe_grouped_gemm1_swiglu(quant_mode, x, x_sf, opts->x_row_stride, &plan, w1, w1_sf, w1_alpha, H, I,
-                               opts->swiglu_alpha, opts->swiglu_beta, opts->swiglu_limit, opts->fc2_input_scale, y1,
-                               y1_sf, stream);
+  s = moe_grouped_gemm1_act(quant_mode, x, x_sf, opts->x_row_stride, &plan, w1, w1_sf, w1_alpha, H, I,
+                            opts->activation, opts->swiglu_alpha, opts->swiglu_beta, opts->swiglu_limit,
+                            opts->situ_beta, opts->situ_linear_beta, opts->fc2_input_scale, y1, y1_sf,
+                            stream);
   if (s != MOE_OK) return s;
   if (mark(2) != hipSuccess) return MOE_ERR_DEVICE;
   if (fused) {

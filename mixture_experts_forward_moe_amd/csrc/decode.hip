@@ -66,7 +66,7 @@ struct DecArgs {
   const uint8_t* w2_sf;
   const float* w2_alpha;
   int H, I;
-  float sw_alpha, sw_beta, sw_limit;
+  GateAct act;          // FC1 activation
   uint16_t* y1;          // [slots, I]
   uint16_t* y2;          // [slots, H]
   int* counters;         // the decode counter block: one done count per 64 columns, zero between calls
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
         const float g = sum16(ag[p]);
         const float u = sum16(au[p]);
         if (ch == 0) {
-          const float y = swiglu_f32(g * al, u * al, a.sw_alpha, a.sw_beta, a.sw_limit);
+          const float y = gated_act_f32(g * al, u * al, a.act);
           a.y1[(int64_t)(slot0 + r0) * a.I + col + 16 * p] = f32_to_bf16(y);
         }
       }
@@ -696,9 +696,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   a.w2_alpha = p.w2_alpha;
   a.H = p.H;
   a.I = p.I;
-  a.sw_alpha = p.swiglu_alpha;
-  a.sw_beta = p.swiglu_beta;
-  a.sw_limit = p.swiglu_limit;
+  a.act = p.act;
   a.y1 = p.y1;
   a.y2 = p.y2;
   a.counters = p.counters;

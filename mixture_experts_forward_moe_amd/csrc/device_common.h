@@ -130,3 +130,31 @@ DEV float swiglu_f32(float g, float u, float alpha, float beta, float limit) {
   float sig = 1.0f / (1.0f + expf(-alpha * gc));
   return gc * sig * (uc + beta);
 }
+
+// The gated FC1 activation ("flashinfer.fused_moe.cute_dsl_fused_moe",
+// Parameters activation_type, swiglu_*, situ_beta, situ_linear_beta), one
+// block of kernel arguments shared by every GEMM1 epilogue.
+enum { ACT_SWIGLU = 0, ACT_GEGLU_TANH = 1, ACT_SITU = 2 };
+struct GateAct {
+  int kind;                  // ACT_*
+  float alpha, beta, limit;  // SwiGLU
+  float situ_beta;           // SiTU gate: situ_beta * tanh(g / situ_beta) * sigmoid(g)
+  float situ_lin;            // SiTU up-branch clamp situ_lin * tanh(u / situ_lin); 0 = none
+};
+
+// y = act(g, u) in fp32 with accurate expf / tanhf and correctly rounded
+// divides, before the single bf16 rounding of y1.
+//   SwiGLU: as above.  GeGLU-tanh: g/2 * (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) * u.
+//   SiTU: b tanh(g/b) sigmoid(g) * u', u' = u or c tanh(u/c).
+DEV float gated_act_f32(float g, float u, const GateAct& p) {
+  if (p.kind == ACT_GEGLU_TANH) {
+    const float z = 0.7978845608028654f * (g + 0.044715f * g * g * g);
+    return 0.5f * g * (1.0f + tanhf(z)) * u;
+  }
+  if (p.kind == ACT_SITU) {
+    const float gate = p.situ_beta * tanhf(g / p.situ_beta) / (1.0f + expf(-g));
+    const float up = p.situ_lin > 0.0f ? p.situ_lin * tanhf(u / p.situ_lin) : u;
+    return gate * up;
+  }
+  return swiglu_f32(g, u, p.alpha, p.beta, p.limit);
+}

@@ -58,7 +58,7 @@ struct KArgs {
   const int32_t* offsets;
   int El, tile, top_k;
   int m_tiles, n_tiles, total_tiles;
-  float sw_alpha, sw_beta, sw_limit;
+  GateAct act;          // FC1 activation
   const float* fc2_scale;
   void* Y;              // y1 codes / y1 bf16 / y2 bf16
   uint8_t* Y_sf;
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
         float g = acc[m][0][i] * alpha;
         float u = acc[m][1][i] * alpha;
         // y1 is rounded once to bf16; requantisation starts from that value
-        y[m][i] = bf16_to_f32(f32_to_bf16(swiglu_f32(g, u, a.sw_alpha, a.sw_beta, a.sw_limit)));
+        y[m][i] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
       }
     if constexpr (MODE == M_W4A16) {
       uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
@@ -479,9 +479,7 @@ hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
   a.n_out = p.I;
   a.n_tiles = p.I / 64;
   a.total_tiles = a.m_tiles * a.n_tiles;
-  a.sw_alpha = p.swiglu_alpha;
-  a.sw_beta = p.swiglu_beta;
-  a.sw_limit = p.swiglu_limit;
+  a.act = p.act;
   a.fc2_scale = p.fc2_input_scale;
   a.Y = p.y1;
   a.Y_sf = p.y1_sf;

@@ -83,7 +83,7 @@ struct XArgs {
   const int32_t* tile_limit;
   const int32_t* num_tiles;
   int top_k;
-  float sw_alpha, sw_beta, sw_limit;
+  GateAct act;          // FC1 activation
   void* Y;              // y1 E4M3 codes / y2 bf16
   uint8_t* Y_sf;        // y1 E8M0 scales
   const float* topk_w;
@@ -286,7 +286,7 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
           const float g = acc[m][n][i] * alpha;
           const float u = acc[m][n + 2][i] * alpha;
           // y1 is rounded once to bf16; requantisation starts from that value
-          y[n] = bf16_to_f32(f32_to_bf16(swiglu_f32(g, u, a.sw_alpha, a.sw_beta, a.sw_limit)));
+          y[n] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
         }
         const float am = warp_max16(fmaxf(fabsf(y[0]), fabsf(y[1])));
         const uint32_t code = mx_scale_code(am, 8);
@@ -434,9 +434,7 @@ hipError_t launch_gemm1_mx(const Gemm1Params& p, hipStream_t stream) {
   a.I = p.I;
   a.n_out = p.I;
   a.n_blocks = p.I / 128;
-  a.sw_alpha = p.swiglu_alpha;
-  a.sw_beta = p.swiglu_beta;
-  a.sw_limit = p.swiglu_limit;
+  a.act = p.act;
   a.Y = p.y1;
   a.Y_sf = p.y1_sf;
   return launch<1, false>(a, p.plan->max_tiles, stream);

@@ -34,7 +34,7 @@
 //    branch.
 //  - LDS layouts, swizzled per 16-byte chunk so that the operand reads are
 //    (nearly) bank-conflict free: activations [slot][4 chunks], chunk c at
-//    c ^ sa(slot); codes [row][4 chunks], chunk c at c ^ ((row >> 1) & 3);
+//    c ^ sa(slot); codes [row][4 chunks], chunk c at c ^ ((row >> 2) & 3);
 //    scales [row][8 bytes].
 //  - reduction order: in a stage lane group q takes K [8q, 8q + 8), one
 //    dword of codes under one E4M3 block scale.
@@ -79,7 +79,7 @@ struct WArgs {
   const int32_t* tile_limit;
   const int32_t* num_tiles;
   int top_k;
-  float sw_alpha, sw_beta, sw_limit;
+  GateAct act;          // FC1 activation
   void* Y;
   const float* topk_w;
   float rsf;
@@ -89,7 +89,10 @@ struct WArgs {
 // activation chunk swizzle (depends on slot & 15 only, so that the 16 rows
 // of an MFMA tile hit 16 distinct 16-byte bank groups)
 DEV int sa(int slot) { return (((slot & 15) >> 1) ^ ((slot & 15) >> 3)) & 3; }
-DEV int sb(int row) { return (row >> 1) & 3; }
+// code chunk swizzle: the 4 rows r, r+4, r+8, r+12 of a 16-row group (64 B
+// per row, so they share banks) get 4 distinct chunks, and a wavefront's
+// dword reads of one stage hit 64 distinct banks
+DEV int sb(int row) { return (row >> 2) & 3; }
 
 template <int GEMM, bool ATOMIC, int MTV>
 DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, int nb) {
@@ -282,7 +285,7 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
           const float g = acc[m][n][i] * alpha;
           const float u = acc[m][n + 2][i] * alpha;
           // y1 is rounded once to bf16; requantisation starts from that value
-          y[m][i] = bf16_to_f32(f32_to_bf16(swiglu_f32(g, u, a.sw_alpha, a.sw_beta, a.sw_limit)));
+          y[m][i] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
         }
       uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
 #pragma unroll
@@ -414,9 +417,7 @@ hipError_t launch_gemm1_wide(const Gemm1Params& p, hipStream_t stream) {
   a.I = p.I;
   a.n_out = p.I;
   a.n_blocks = p.I / 128;
-  a.sw_alpha = p.swiglu_alpha;
-  a.sw_beta = p.swiglu_beta;
-  a.sw_limit = p.swiglu_limit;
+  a.act = p.act;
   a.Y = p.y1;
   return launch<1, false>(a, p.plan->max_tiles, stream);
 }

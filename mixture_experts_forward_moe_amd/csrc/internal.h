@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "../../include/moe.h"
+#include "device_common.h"
 
 namespace moe {
 
@@ -27,7 +28,7 @@ struct Gemm1Params {
   const uint8_t* w1_sf;
   const float* w1_alpha;
   int H, I;
-  float swiglu_alpha, swiglu_beta, swiglu_limit;
+  GateAct act;
   const float* fc2_input_scale;
   void* y1;
   uint8_t* y1_sf;
@@ -78,7 +79,7 @@ struct DecodeParams {
   const uint8_t *w2, *w2_sf;
   const float* w2_alpha;
   int H, I;
-  float swiglu_alpha, swiglu_beta, swiglu_limit;
+  GateAct act;
   uint16_t* y1;
   uint16_t* y2;
   int* counters;  // the decode counter block (DEC_COUNTER_BYTES), zero between calls

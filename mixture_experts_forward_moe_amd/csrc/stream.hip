@@ -48,7 +48,7 @@ struct StreamArgs {
   const int32_t* tile_limit;
   const int32_t* num_tiles;
   int top_k, M;
-  float sw_alpha, sw_beta, sw_limit;
+  GateAct act;          // FC1 activation
   uint16_t* Y;          // y1 (GEMM1) or y2 (GEMM2 without finalize)
   const float* topk_w;
   float rsf;
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(ST_THREADS) void gemm1_stream_kernel(const StreamAr
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int row = 4 * q + i;
-        const float y = swiglu_f32(ag[i] * al, au[i] * al, a.sw_alpha, a.sw_beta, a.sw_limit);
+        const float y = gated_act_f32(ag[i] * al, au[i] * al, a.act);
         if (row < valid) a.Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(y);
       }
     }
@@ -274,9 +274,7 @@ hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream) {
   a.num_tiles = p.plan->num_tiles;
   a.top_k = p.plan->top_k;
   a.M = p.plan->M;
-  a.sw_alpha = p.swiglu_alpha;
-  a.sw_beta = p.swiglu_beta;
-  a.sw_limit = p.swiglu_limit;
+  a.act = p.act;
   a.Y = reinterpret_cast<uint16_t*>(p.y1);
   const int P = tile_stride(p.plan);
   if (P == 0) return hipSuccess;

@@ -53,6 +53,7 @@ class DeviceProblem:
                         self.w2_sf, self.w2_alpha, p.num_experts, p.top_k, p.num_local_experts,
                         p.local_expert_offset, p.mode, out, p.H, p.I, tile=tile,
                         swiglu_alpha=p.swiglu_alpha, swiglu_beta=p.swiglu_beta, swiglu_limit=p.swiglu_limit,
+                        activation=p.activation, situ_beta=p.situ_beta, situ_linear_beta=p.situ_linear_beta,
                         fc2_input_scale=self.fc2, routed_scaling_factor=p.routed_scaling_factor, **kw)
         return out
 

@@ -97,6 +97,36 @@ def test_gemm_argument_checks():
     assert L.moe_finalize(F, p, F, 100, 1.0, 0, F, None) == UNSUPPORTED
 
 
+def test_activation_argument_checks():
+    """The FC1 activation rules are checked on the host, before any launch."""
+    L = moe.lib()
+    p = ctypes.byref(_plan())
+    F = FAKE
+    g = lambda act, a=1.0, b=0.0, lim=moe.FLT_MAX, sb=0.0, slb=0.0: L.moe_grouped_gemm1_act(
+        0, F, None, 0, p, F, F, F, 256, 512, act, a, b, lim, sb, slb, None, F, None, None)
+    assert g(moe.ACT_RELU2) == UNSUPPORTED                         # non-gated GEMM1 is not built
+    assert g(7) == INVALID                                         # unknown activation
+    assert g(moe.ACT_GEGLU_TANH, a=1.702) == INVALID               # GeGLU takes no SwiGLU parameters
+    assert g(moe.ACT_GEGLU_TANH, lim=7.0) == INVALID
+    assert g(moe.ACT_GEGLU_TANH, sb=0.5) == INVALID                # ... nor SiTU ones
+    assert g(moe.ACT_SWIGLU, sb=0.5, b=1.0) == INVALID             # SiTU with SwiGLU parameters
+    assert g(moe.ACT_SWIGLU, slb=0.5) == INVALID                   # up clamp without SiTU
+    assert g(moe.ACT_SWIGLU, sb=-1.0) == INVALID
+    assert g(moe.ACT_SWIGLU, sb=float("inf")) == INVALID
+    assert g(moe.ACT_SWIGLU, sb=float("nan")) == INVALID
+    assert g(moe.ACT_SWIGLU, sb=0.5, slb=-0.1) == INVALID
+    assert g(moe.ACT_SWIGLU, lim=0.0) == INVALID
+    # the forward checks the same rules before it enqueues anything
+    o = moe.make_opts(activation=moe.ACT_RELU2)
+    o.workspace = 0x10000
+    o.workspace_bytes = 1 << 30
+    args = (F, None, F, F, F, F, F, F, F, F, 8, 2, 8, 0, 0, F, 16, 256, 512, ctypes.byref(o), None)
+    assert L.moe_forward(*args) == UNSUPPORTED
+    o.activation = moe.ACT_GEGLU_TANH
+    o.swiglu_limit = 7.0
+    assert L.moe_forward(*args) == INVALID
+
+
 def test_forward_argument_checks():
     L = moe.lib()
     F = FAKE

@@ -28,6 +28,15 @@ CASES = {
     "mx_offset": (oracle.MXFP8_MXFP4, dict(M=45, H=512, I=256, E=16, El=6, k=4, seed=47, offset=9)),
     "mx_tall": (oracle.MXFP8_MXFP4, dict(M=450, H=512, I=512, E=8, El=6, k=3, seed=54, offset=1,
                                          router_bias_std=0.7, swiglu_limit=2.0)),
+    # the other gated FC1 activations through every GEMM1 kernel: GeGLU-tanh and SiTU (with and
+    # without the up-branch clamp)
+    "w4a16_geglu": (oracle.W4A16, dict(M=70, H=512, I=384, E=4, El=4, k=3, seed=55,
+                                       activation=oracle.ACT_GEGLU_TANH)),
+    "w4a16_situ": (oracle.W4A16, dict(M=60, H=512, I=512, E=8, El=8, k=3, seed=56, situ_beta=0.1,
+                                      situ_linear_beta=0.08)),
+    "w4a4_situ": (oracle.W4A4, dict(M=40, H=256, I=256, E=8, El=8, k=2, seed=57, situ_beta=0.1)),
+    "mx_geglu": (oracle.MXFP8_MXFP4, dict(M=450, H=512, I=512, E=8, El=6, k=3, seed=58, offset=1,
+                                          router_bias_std=0.7, activation=oracle.ACT_GEGLU_TANH)),
 }
 
 _cache = {}
@@ -69,8 +78,9 @@ def test_gemm1_and_gemm2_stages(name, tile):
     s1, dt1, s1sf = oracle.y1_shapes(p.mode, slots, p.I)
     y1 = torch.zeros(s1, dtype=torch.int16 if dt1 == np.uint16 else torch.uint8, device="cuda")
     y1_sf = None if s1sf is None else torch.zeros(s1sf, dtype=torch.uint8, device="cuda")
-    moe.moe_grouped_gemm1_swiglu(p.mode, d.x, d.x_sf, plan, d.w1, d.w1_sf, d.w1_alpha, p.H, p.I, y1, y1_sf,
-                                 p.swiglu_alpha, p.swiglu_beta, p.swiglu_limit, d.fc2)
+    moe.moe_grouped_gemm1_act(p.mode, d.x, d.x_sf, plan, d.w1, d.w1_sf, d.w1_alpha, p.H, p.I, y1, y1_sf,
+                              p.activation, p.swiglu_alpha, p.swiglu_beta, p.swiglu_limit, p.situ_beta,
+                              p.situ_linear_beta, d.fc2)
     torch.cuda.synchronize()
     valid = rplan.permuted_to_expanded >= 0
     gq = host(y1, dt1)[valid]
@@ -174,6 +184,13 @@ def decode_case(case):
     elif case == "one_token":
         wl = synth.small_workload(oracle.W4A16, 1, 2048, 512, 16, 16, 4, 53)
         raw = synth.make_raw(wl)
+    elif case == "geglu":
+        wl = synth.small_workload(oracle.W4A16, 9, 2048, 1536, 64, 16, 6, 59, offset=8,
+                                  activation=oracle.ACT_GEGLU_TANH)
+        raw = synth.make_raw(wl)
+    elif case == "situ":
+        wl = synth.small_workload(oracle.W4A16, 8, 2048, 1024, 32, 32, 4, 60, situ_beta=0.2, situ_linear_beta=0.1)
+        raw = synth.make_raw(wl)
     else:  # "offset_swiglu": a local window of the experts, clamped SwiGLU
         wl = synth.small_workload(oracle.W4A16, 9, 2048, 1536, 64, 16, 6, 54, offset=24, swiglu_limit=0.4,
                                   swiglu_alpha=1.702, swiglu_beta=1.0)
@@ -181,7 +198,7 @@ def decode_case(case):
     return oracle.quantize_problem(raw)
 
 
-@pytest.mark.parametrize("case", ["no_local_routes", "hot_experts", "one_token", "offset_swiglu"])
+@pytest.mark.parametrize("case", ["no_local_routes", "hot_experts", "one_token", "offset_swiglu", "geglu", "situ"])
 def test_decode_path_edge_cases(case):
     """Decode-sized batches (tile 16) through the single-launch path: no
     local route at all, experts with several tiles and a ragged last tile,
