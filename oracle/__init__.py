@@ -46,6 +46,7 @@ class _Moe(ctypes.Structure):
         ("swiglu_alpha", ctypes.c_float), ("swiglu_beta", ctypes.c_float), ("swiglu_limit", ctypes.c_float),
         ("fc2_input_scale", ctypes.c_float), ("routed_scaling_factor", ctypes.c_float),
         ("activation", ctypes.c_int), ("situ_beta", ctypes.c_float), ("situ_linear_beta", ctypes.c_float),
+        ("w1_alpha_up", ctypes.c_void_p), ("per_token_scale", ctypes.c_void_p),
     ]
 
 
@@ -264,13 +265,16 @@ class Problem:
     activation: int = 0          # ACT_SWIGLU (SiTU when situ_beta > 0) | ACT_GEGLU_TANH
     situ_beta: float = 0.0
     situ_linear_beta: float = 0.0
+    w1_alpha_up: np.ndarray | None = None      # fp32 [E_l]: the up half's own scale (None: w1_alpha)
+    per_token_scale: np.ndarray | None = None  # fp32 [M], W4A4: GEMM1 input row scale
 
     def struct(self) -> _Moe:
         s = _Moe()
         s.mode, s.M, s.H, s.I = self.mode, self.M, self.H, self.I
         s.top_k, s.num_experts, s.num_local_experts = self.top_k, self.num_experts, self.num_local_experts
         s.local_expert_offset = self.local_expert_offset
-        for name in ("x", "x_sf", "topk_ids", "topk_weights", "w1", "w1_sf", "w1_alpha", "w2", "w2_sf", "w2_alpha"):
+        for name in ("x", "x_sf", "topk_ids", "topk_weights", "w1", "w1_sf", "w1_alpha", "w2", "w2_sf", "w2_alpha",
+                     "w1_alpha_up", "per_token_scale"):
             a = getattr(self, name)
             if a is not None:
                 assert a.flags["C_CONTIGUOUS"], name

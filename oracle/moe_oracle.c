@@ -373,6 +373,8 @@ typedef struct {
   int activation;         /* ORC_ACT_SWIGLU (SwiGLU, or SiTU when situ_beta > 0) | ORC_ACT_GEGLU_TANH */
   float situ_beta;        /* > 0 selects SiTU; 0 = unset */
   float situ_linear_beta; /* > 0: SiTU tanh clamp of the up branch; 0 = unset */
+  const float* w1_alpha_up;     /* NULL, or fp32 [E_l]: the up half's own scale */
+  const float* per_token_scale; /* NULL, or fp32 [M] (W4A4): GEMM1 input row scale */
 } orc_moe_t;
 
 static int sf_block(int mode) { return mode == ORC_MXFP8_MXFP4 ? 32 : 16; }
@@ -480,17 +482,36 @@ static float scale_acc(double acc, float alpha) {
   return r;
 }
 
+/* Gate and up values of token t through local expert le from their fp64
+ * sums: the accumulator in fp32 times the expert's gate scale (w1_alpha) or
+ * up scale (w1_alpha_up when given, "flashinfer.fused_moe.
+ * alphamoe_nvfp4_routed_moe", Parameters output1_scale_gate_scalar /
+ * output1_scale_scalar), then times the token's per_token_scale when given
+ * ("flashinfer.fused_moe.cute_dsl_fused_moe", Parameters per_token_scale):
+ * separate fp32 multiplies in that order. */
+static void gate_up(const orc_moe_t* p, int le, int64_t t, double G, double U, float* g, float* u) {
+  float gv = scale_acc(G, p->w1_alpha[le]);
+  float uv = scale_acc(U, p->w1_alpha_up ? p->w1_alpha_up[le] : p->w1_alpha[le]);
+  if (p->per_token_scale) {
+    float s = p->per_token_scale[t];
+    gv = gv * s;
+    uv = uv * s;
+  }
+  *g = gv;
+  *u = uv;
+}
+
 /* FC1 output of one row: y1 (bf16, rounded once), then the GEMM2 input as
  * the mode stores it (bf16 | NVFP4 with fc2_input_scale | MXFP8) and its
  * decoded values a2 (for W4A4 without the global scale, which is part of
  * w2_alpha). */
-static void swiglu_row_and_requant(const orc_moe_t* p, int le, const double* G, const double* U,
+static void swiglu_row_and_requant(const orc_moe_t* p, int le, int64_t t, const double* G, const double* U,
                                    uint16_t* y1_bf16, uint8_t* y1q, uint8_t* y1sf, double* a2) {
   int I = p->I;
   float* y = (float*)malloc((size_t)I * sizeof(float));
   for (int j = 0; j < I; j++) {
-    float g = scale_acc(G[j], p->w1_alpha[le]);
-    float u = scale_acc(U[j], p->w1_alpha[le]);
+    float g, u;
+    gate_up(p, le, t, G[j], U[j], &g, &u);
     uint16_t b = orc_bf16_round(gated_act(p, g, u));
     if (y1_bf16) y1_bf16[j] = b;
     y[j] = orc_bf16_value(b);
@@ -542,7 +563,7 @@ void orc_gemm1_route(const orc_moe_t* p, int64_t t, int le, uint16_t* y1_bf16, u
     }
     free(w);
   }
-  swiglu_row_and_requant(p, le, G, U, y1_bf16, y1q, y1sf, a2);
+  swiglu_row_and_requant(p, le, t, G, U, y1_bf16, y1q, y1sf, a2);
   free(a);
   free(G);
   free(U);
@@ -687,7 +708,7 @@ void orc_forward_plan(const orc_moe_t* p, int tile, int32_t* e2p, int32_t* p2e,
           yq = (uint8_t*)y1 + slot * I;
           ys = y1_sf + slot * (I / 32);
         }
-        swiglu_row_and_requant(p, le, G, U, yb, yq, ys, a2);
+        swiglu_row_and_requant(p, le, t, G, U, yb, yq, ys, a2);
         for (int c = 0; c < H; c++)
           y2[slot * H + c] = orc_bf16_round(scale_acc(dot(a2, wd2 + (int64_t)c * I, I), p->w2_alpha[le]));
       }
@@ -725,8 +746,8 @@ float orc_fc2_input_scale(const orc_moe_t* p) {
         if (p->topk_ids[r] - p->local_expert_offset != le) continue;
         dequant_x_row(p, r / k, a);
         for (int n = 0; n < I; n++) {
-          float g = scale_acc(dot(a, wd1 + (int64_t)n * H, H), p->w1_alpha[le]);
-          float u = scale_acc(dot(a, wd1 + (int64_t)(I + n) * H, H), p->w1_alpha[le]);
+          float g, u;
+          gate_up(p, le, r / k, dot(a, wd1 + (int64_t)n * H, H), dot(a, wd1 + (int64_t)(I + n) * H, H), &g, &u);
           uint16_t b = orc_bf16_round(gated_act(p, g, u));
           float v = fabsf(orc_bf16_value(b));
           if (v > local) local = v;

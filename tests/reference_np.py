@@ -154,8 +154,13 @@ def forward_tokens(p, tokens):
             W1d, W2d = w1d_cache[le]
             gu = W1d @ a
             al1 = np.float32(p.w1_alpha[le])
+            alu = al1 if getattr(p, "w1_alpha_up", None) is None else np.float32(p.w1_alpha_up[le])
             g = (gu[:I].astype(np.float32) * al1).astype(np.float32)
-            u = (gu[I:].astype(np.float32) * al1).astype(np.float32)
+            u = (gu[I:].astype(np.float32) * alu).astype(np.float32)
+            if getattr(p, "per_token_scale", None) is not None:
+                pts = np.float32(p.per_token_scale[t])
+                g = (g * pts).astype(np.float32)
+                u = (u * pts).astype(np.float32)
             y1 = bf16_vals(to_bf16_bits(gated_act(p, g, u)))
             if p.mode == W4A16:
                 a2 = y1

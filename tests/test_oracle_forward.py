@@ -150,6 +150,50 @@ def test_situ_pins():
     assert oracle.situ(1e-4, 2e-4, 0.5, 0.25) == pytest.approx(oracle.swiglu(1e-4, 2e-4), rel=1e-6)
 
 
+def _scaled_problem(mode, seed, up=True, per_token=False):
+    p = _problem(mode, M=9, H=64, I=64, E=8, El=6, k=3, seed=seed, offset=1)
+    rng = np.random.default_rng(seed)
+    if up:
+        p.w1_alpha_up = (p.w1_alpha * rng.uniform(0.5, 2.0, p.w1_alpha.shape)).astype(np.float32)
+    if per_token:
+        p.per_token_scale = rng.uniform(0.25, 4.0, p.M).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("mode,per_token", [(oracle.W4A16, False), (oracle.W4A4, True), (oracle.MXFP8_MXFP4, False)])
+def test_separate_up_scale_and_per_token_scale(mode, per_token):
+    """The up half's own per-expert scale and the W4A4 per-token input row
+    scale: against the independent torch pipeline, and plan-based equal to
+    per-token evaluation bit for bit."""
+    p = _scaled_problem(mode, 61 + mode, up=True, per_token=per_token)
+    tokens = np.arange(p.M)
+    got = oracle.forward_tokens(p, tokens)
+    _close_bf16(got, ref.forward_tokens(p, tokens))
+    _, _, _, _, out = oracle.forward_plan(p, 4)
+    assert np.array_equal(out, got)
+
+
+def test_neutral_scales_change_nothing():
+    # an up scale equal to w1_alpha, or a per-token scale of ones, is no scale at all
+    for mode in (oracle.W4A16, oracle.W4A4):
+        p = _problem(mode, M=8, H=64, I=64, E=4, El=4, k=2, seed=63)
+        want = oracle.forward_tokens(p, np.arange(p.M))
+        p.w1_alpha_up = p.w1_alpha.copy()
+        if mode == oracle.W4A4:
+            p.per_token_scale = np.ones(p.M, np.float32)
+        assert np.array_equal(oracle.forward_tokens(p, np.arange(p.M)), want)
+
+
+def test_power_of_two_up_scale_scales_y1_exactly():
+    # SwiGLU at its defaults is linear in the up branch: doubling the up scale doubles y1 exactly
+    p = _problem(oracle.W4A16, M=6, H=64, I=32, E=4, El=4, k=2, seed=64)
+    _, y1, _, _, _ = oracle.forward_plan(p, 4)
+    p.w1_alpha_up = (p.w1_alpha * np.float32(2.0)).astype(np.float32)
+    plan, y1b, _, _, _ = oracle.forward_plan(p, 4)
+    valid = plan.permuted_to_expanded >= 0
+    assert np.array_equal(synth.bf16_to_f32(y1[valid]) * 2, synth.bf16_to_f32(y1b[valid]))
+
+
 def test_power_of_two_w2_alpha_scales_y2_exactly():
     p = _problem(oracle.W4A16, M=8, H=64, I=32, E=4, El=4, k=2, seed=32)
     _, _, _, y2, _ = oracle.forward_plan(p, 8)
