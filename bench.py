@@ -121,7 +121,16 @@ def _opts(moe, wl, ws, tile, fc2=None, **kw):
                          situ_linear_beta=wl.situ_linear_beta, fc2_input_scale=fc2, **kw)
 
 
-def time_graph(wl, steps: int, warmup: int, copies: int):
+def _scale_kw(g, scaled: bool):
+    """Options of the scaled variant: the up half with its own per-expert
+    scale (1.5x the gate's) and routed_scaling_factor 1.75."""
+    if not scaled:
+        return {}
+    w1a = g.copies[0][5]
+    return dict(w1_alpha_up=(w1a * 1.5).contiguous(), routed_scaling_factor=1.75)
+
+
+def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False):
     """Times `steps` forwards replayed from a HIP graph that holds `copies`
     forwards, one per resident input copy (no host work between launches).
     HIP events on the replay stream bracket the timed replays."""
@@ -133,7 +142,8 @@ def time_graph(wl, steps: int, warmup: int, copies: int):
     tile = moe.default_tile(wl.M, wl.top_k, E, wl.mode)
     ws = torch.zeros(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.M, H), dtype=torch.int16, device="cuda")
-    opts = _opts(moe, wl, ws, tile, fc2=g.fc2)
+    skw = _scale_kw(g, scaled)
+    opts = _opts(moe, wl, ws, tile, fc2=g.fc2, **skw)
 
     def step(i):
         x, ids, w, w1, w1s, w1a, w2, w2s, w2a, xs = g.copies[i % len(g.copies)]
@@ -168,7 +178,7 @@ def time_graph(wl, steps: int, warmup: int, copies: int):
                 local_routes=routes, active_experts=active)
 
 
-def time_phases(wl, steps: int, warmup: int, copies: int):
+def time_phases(wl, steps: int, warmup: int, copies: int, scaled: bool = False):
     """Times `steps` eager forwards, then the same steps again with HIP
     events that moe_forward records between its launches on the same
     stream (per-kernel durations)."""
@@ -186,8 +196,9 @@ def time_phases(wl, steps: int, warmup: int, copies: int):
         for e in row:
             e.record()
     torch.cuda.synchronize()
-    opts = _opts(moe, wl, ws, tile, fc2=g.fc2)
-    opts_ev = [_opts(moe, wl, ws, tile, fc2=g.fc2, phase_events=events[i]) for i in range(steps)]
+    skw = _scale_kw(g, scaled)
+    opts = _opts(moe, wl, ws, tile, fc2=g.fc2, **skw)
+    opts_ev = [_opts(moe, wl, ws, tile, fc2=g.fc2, phase_events=events[i], **skw) for i in range(steps)]
 
     def step(i, o):
         x, ids, w, w1, w1s, w1a, w2, w2s, w2a, xs = g.copies[i % len(g.copies)]
@@ -417,26 +428,31 @@ def main():
                           "weight_bytes": wb, "weights_hbm_frac": wb / (r3["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "note": note}
     if not args.no_secondary:
-        # the other gated FC1 activations on the decode and prefill workloads: the decode forward in
-        # graph replay (same roofline unit as the headline) and the prefill GEMM1 with per-kernel events
+        # the other FC1 epilogues on the decode and prefill workloads (GeGLU-tanh, SiTU, and SwiGLU with
+        # the up half's own scale and routed_scaling_factor 1.75): the decode forward in graph replay
+        # (same roofline unit as the headline) and the prefill GEMM1 with per-kernel events
         import dataclasses
         acts = {}
-        for name, kw in (("geglu_tanh", dict(activation=1)), ("situ", dict(situ_beta=0.5, situ_linear_beta=1.0))):
+        for name, kw in (("geglu_tanh", dict(activation=1)), ("situ", dict(situ_beta=0.5, situ_linear_beta=1.0)),
+                         ("swiglu_scaled", dict())):
+            scaled = name == "swiglu_scaled"
             wd = dataclasses.replace(wl, **kw)
             log(f"bench: {wd.name} with {name}: {max(20, args.steps // 4)} steps (graph replay)")
-            rd = time_graph(wd, max(20, args.steps // 4), max(4, args.warmup // 4), args.copies)
+            rd = time_graph(wd, max(20, args.steps // 4), max(4, args.warmup // 4), args.copies, scaled=scaled)
             fd = by["forward"] / (rd["gpu_ms_per_step"] * 1e-3) / 1e9
             wp = dataclasses.replace(synth.WORKLOADS["w4a16_prefill"], swiglu_limit=float(np.finfo(np.float32).max),
                                      **kw)
-            rp = time_phases(wp, 10, 3, args.copies)
+            rp = time_phases(wp, 10, 3, args.copies, scaled=scaled)
             g1 = 4.0 * wp.H * wp.I * rp["local_routes"] / (rp["phase_ms"]["gemm1"] * 1e-3) / 1e12
+            if scaled:
+                kw = {"w1_alpha_up": "1.5 x w1_alpha", "routed_scaling_factor": 1.75}
             acts[name] = {"params": kw, "decode_ms_per_forward": rd["gpu_ms_per_step"], "decode_hbm_frac": fd / HBM_PEAK_GBS,
                           "prefill_gemm1_ms": rp["phase_ms"]["gemm1"], "prefill_gemm1_mfma_frac": g1 / BF16_PEAK_TFLOPS}
         acts["swiglu"] = {"decode_ms_per_forward": f_ms, "decode_hbm_frac": f_gbs / HBM_PEAK_GBS,
                           "prefill_gemm1_ms": line["prefill"]["phase_ms"]["gemm1"],
                           "prefill_gemm1_mfma_frac": line["prefill"]["gemm1_mfma_frac"],
                           "note": "prefill with SwiGLU limit 7 (its workload); the others without a limit"}
-        line["activations"] = acts
+        line["epilogue_variants"] = acts
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(wl)

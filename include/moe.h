@@ -175,7 +175,17 @@ typedef enum moe_activation {
 } moe_activation_t;
 
 /* moe_grouped_gemm1_act: moe_grouped_gemm1_swiglu with the FC1 activation
- * chosen by `activation` (same Parameters of cute_dsl_fused_moe):
+ * chosen by `activation`, and two optional scales of the accumulator:
+ *   w1_alpha_up: device fp32 [E_l], the up half's own per-expert scale
+ *     (gate rows take w1_alpha; "flashinfer.fused_moe.
+ *     alphamoe_nvfp4_routed_moe", Parameters output1_scale_gate_scalar and
+ *     output1_scale_scalar).  NULL: w1_alpha for both halves.
+ *   per_token_scale: device fp32 [M], W4A4 only: the token's input row scale
+ *     ("flashinfer.fused_moe.cute_dsl_fused_moe", Parameters
+ *     per_token_scale), applied after the expert scale:
+ *     g = fp32(fp32(acc_g) * w1_alpha[e]) * per_token_scale[t], likewise u.
+ *     NULL: none.  Non-NULL outside W4A4: MOE_ERR_INVALID_ARGUMENT.
+ * The activations (same Parameters of cute_dsl_fused_moe):
  *   MOE_ACT_SWIGLU, situ_beta == 0: the SwiGLU above.
  *   MOE_ACT_SWIGLU, situ_beta  > 0: SiTU,
  *       y1 = situ_beta * tanh(g / situ_beta) * sigmoid(g) * u',
@@ -189,10 +199,11 @@ typedef enum moe_activation {
  * parameters.  MOE_ERR_UNSUPPORTED: MOE_ACT_RELU2. */
 moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const uint8_t* x_sf,
                                    int64_t x_row_stride, const moe_plan_t* plan, const uint8_t* w1,
-                                   const uint8_t* w1_sf, const float* w1_alpha, int H, int I,
-                                   int activation, float swiglu_alpha, float swiglu_beta, float swiglu_limit,
-                                   float situ_beta, float situ_linear_beta, const float* fc2_input_scale,
-                                   void* y1, uint8_t* y1_sf, moe_stream_t stream);
+                                   const uint8_t* w1_sf, const float* w1_alpha, const float* w1_alpha_up, int H,
+                                   int I, int activation, float swiglu_alpha, float swiglu_beta,
+                                   float swiglu_limit, float situ_beta, float situ_linear_beta,
+                                   const float* fc2_input_scale, const float* per_token_scale, void* y1,
+                                   uint8_t* y1_sf, moe_stream_t stream);
 
 /* moe_grouped_gemm2: for every valid slot s of local expert e, multiply the
  * stored FC1 output (decoded as moe_grouped_gemm1_swiglu wrote it; in W4A4
@@ -248,6 +259,8 @@ typedef struct moe_opts {
                                     moe_grouped_gemm1_act) */
   float situ_beta;               /* default 0 (SwiGLU); > 0 selects SiTU */
   float situ_linear_beta;        /* default 0 (no up-branch clamp) */
+  const float* w1_alpha_up;      /* device fp32 [E_l]: the up half's scale; NULL = w1_alpha */
+  const float* per_token_scale;  /* device fp32 [M], W4A4 only: GEMM1 input row scale; NULL = none */
 } moe_opts_t;
 
 #define MOE_NUM_PHASE_EVENTS 5

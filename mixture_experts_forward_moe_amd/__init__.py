@@ -53,6 +53,7 @@ class Opts(ctypes.Structure):
         ("tile", ctypes.c_int), ("x_row_stride", ctypes.c_int64), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("phase_events", ctypes.c_void_p),
         ("activation", ctypes.c_int), ("situ_beta", ctypes.c_float), ("situ_linear_beta", ctypes.c_float),
+        ("w1_alpha_up", ctypes.c_void_p), ("per_token_scale", ctypes.c_void_p),
     ]
 
 
@@ -74,7 +75,7 @@ def lib() -> ctypes.CDLL:
             "moe_plan_init": ([P, P, SZ, I, I, I, I], I),
             "moe_sort": ([P, I, I, I, I, I, I, P, P], I),
             "moe_grouped_gemm1_swiglu": ([I, P, P, I64, P, P, P, P, I, I, F, F, F, P, P, P, P], I),
-            "moe_grouped_gemm1_act": ([I, P, P, I64, P, P, P, P, I, I, I, F, F, F, F, F, P, P, P, P], I),
+            "moe_grouped_gemm1_act": ([I, P, P, I64, P, P, P, P, P, I, I, I, F, F, F, F, F, P, P, P, P, P], I),
             "moe_grouped_gemm2": ([I, P, P, P, P, P, P, I, I, P, P, F, P, P], I),
             "moe_finalize": ([P, P, P, I, F, I, P, P], I),
             "moe_opts_init": ([P], None),
@@ -206,11 +207,13 @@ def moe_grouped_gemm1_swiglu(mode, x, x_sf, plan: MoePlan, w1, w1_sf, w1_alpha, 
 
 def moe_grouped_gemm1_act(mode, x, x_sf, plan: MoePlan, w1, w1_sf, w1_alpha, H, I, y1, y1_sf=None,
                           activation=ACT_SWIGLU, swiglu_alpha=1.0, swiglu_beta=0.0, swiglu_limit=FLT_MAX,
-                          situ_beta=0.0, situ_linear_beta=0.0, fc2_input_scale=None, x_row_stride=0, stream=None):
+                          situ_beta=0.0, situ_linear_beta=0.0, fc2_input_scale=None, x_row_stride=0, stream=None,
+                          w1_alpha_up=None, per_token_scale=None):
     _check(lib().moe_grouped_gemm1_act(mode, _ptr(x), _ptr(x_sf), x_row_stride, ctypes.byref(plan.c), _ptr(w1),
-                                       _ptr(w1_sf), _ptr(w1_alpha), H, I, activation, swiglu_alpha, swiglu_beta,
-                                       swiglu_limit, situ_beta, situ_linear_beta, _ptr(fc2_input_scale), _ptr(y1),
-                                       _ptr(y1_sf), _stream(stream)), "moe_grouped_gemm1_act")
+                                       _ptr(w1_sf), _ptr(w1_alpha), _ptr(w1_alpha_up), H, I, activation,
+                                       swiglu_alpha, swiglu_beta, swiglu_limit, situ_beta, situ_linear_beta,
+                                       _ptr(fc2_input_scale), _ptr(per_token_scale), _ptr(y1), _ptr(y1_sf),
+                                       _stream(stream)), "moe_grouped_gemm1_act")
 
 
 def moe_grouped_gemm2(mode, y1, y1_sf, plan: MoePlan, w2, w2_sf, w2_alpha, H, I, y2=None, topk_weights=None,
@@ -228,11 +231,13 @@ def moe_finalize(y2, plan: MoePlan, topk_weights, H, out, routed_scaling_factor=
 def make_opts(workspace=None, swiglu_alpha=1.0, swiglu_beta=0.0, swiglu_limit=FLT_MAX, fc2_input_scale=None,
               routed_scaling_factor=1.0, accumulate=False, finalize_mode=FINALIZE_DETERMINISTIC,
               route_order=ROUTE_ORDER_AUTO, tile=0, x_row_stride=0, phase_events=None, activation=ACT_SWIGLU,
-              situ_beta=0.0, situ_linear_beta=0.0) -> Opts:
+              situ_beta=0.0, situ_linear_beta=0.0, w1_alpha_up=None, per_token_scale=None) -> Opts:
     o = Opts()
     lib().moe_opts_init(ctypes.byref(o))
     o.swiglu_alpha, o.swiglu_beta, o.swiglu_limit = swiglu_alpha, swiglu_beta, swiglu_limit
     o.activation, o.situ_beta, o.situ_linear_beta = activation, situ_beta, situ_linear_beta
+    o.w1_alpha_up = None if w1_alpha_up is None else w1_alpha_up.data_ptr()
+    o.per_token_scale = None if per_token_scale is None else per_token_scale.data_ptr()
     o.fc2_input_scale = None if fc2_input_scale is None else fc2_input_scale.data_ptr()
     o.routed_scaling_factor = routed_scaling_factor
     o.accumulate = int(bool(accumulate))

@@ -174,10 +174,11 @@ moe_status_t moe_sort(const int32_t* topk_ids, int M, int top_k, int num_experts
 
 moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const uint8_t* x_sf,
                                    int64_t x_row_stride, const moe_plan_t* plan, const uint8_t* w1,
-                                   const uint8_t* w1_sf, const float* w1_alpha, int H, int I,
-                                   int activation, float swiglu_alpha, float swiglu_beta, float swiglu_limit,
-                                   float situ_beta, float situ_linear_beta, const float* fc2_input_scale,
-                                   void* y1, uint8_t* y1_sf, moe_stream_t stream) {
+                                   const uint8_t* w1_sf, const float* w1_alpha, const float* w1_alpha_up, int H,
+                                   int I, int activation, float swiglu_alpha, float swiglu_beta,
+                                   float swiglu_limit, float situ_beta, float situ_linear_beta,
+                                   const float* fc2_input_scale, const float* per_token_scale, void* y1,
+                                   uint8_t* y1_sf, moe_stream_t stream) {
   if (!mode_ok(mode) || !plan_ok(plan)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status_t s = shape_check(H, I, mode);
   if (s != MOE_OK) return s;
@@ -185,6 +186,7 @@ moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const u
   if (plan->M > 0 && !x) return MOE_ERR_INVALID_ARGUMENT;
   if ((mode == MOE_QUANT_W4A16) != (x_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;   // x_sf None iff w4a16
   if ((mode == MOE_QUANT_W4A4) != (fc2_input_scale != NULL)) return MOE_ERR_INVALID_ARGUMENT;
+  if (per_token_scale && mode != MOE_QUANT_W4A4) return MOE_ERR_INVALID_ARGUMENT;
   if ((mode == MOE_QUANT_W4A16) != (y1_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t row_units = (mode == MOE_QUANT_W4A4) ? H / 2 : H;
   if (x_row_stride != 0 && x_row_stride < row_units) return MOE_ERR_INVALID_ARGUMENT;
@@ -201,9 +203,11 @@ moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const u
   p.w1 = w1;
   p.w1_sf = w1_sf;
   p.w1_alpha = w1_alpha;
+  p.w1_alpha_up = w1_alpha_up;
   p.H = H;
   p.I = I;
   p.fc2_input_scale = fc2_input_scale;
+  p.per_token_scale = per_token_scale;
   p.y1 = y1;
   p.y1_sf = y1_sf;
   if (plan->M == 0) return MOE_OK;
@@ -216,9 +220,9 @@ moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, cons
                                       float swiglu_alpha, float swiglu_beta, float swiglu_limit,
                                       const float* fc2_input_scale, void* y1, uint8_t* y1_sf,
                                       moe_stream_t stream) {
-  return moe_grouped_gemm1_act(mode, x, x_sf, x_row_stride, plan, w1, w1_sf, w1_alpha, H, I, MOE_ACT_SWIGLU,
-                               swiglu_alpha, swiglu_beta, swiglu_limit, 0.0f, 0.0f, fc2_input_scale, y1, y1_sf,
-                               stream);
+  return moe_grouped_gemm1_act(mode, x, x_sf, x_row_stride, plan, w1, w1_sf, w1_alpha, NULL, H, I,
+                               MOE_ACT_SWIGLU, swiglu_alpha, swiglu_beta, swiglu_limit, 0.0f, 0.0f,
+                               fc2_input_scale, NULL, y1, y1_sf, stream);
 }
 
 moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint8_t* y1_sf,
@@ -328,6 +332,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   if (!w1 || !w1_sf || !w1_alpha || !w2 || !w2_sf || !w2_alpha) return MOE_ERR_INVALID_ARGUMENT;
   if ((quant_mode == MOE_QUANT_W4A16) != (x_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
   if ((quant_mode == MOE_QUANT_W4A4) != (opts->fc2_input_scale != NULL)) return MOE_ERR_INVALID_ARGUMENT;
+  if (opts->per_token_scale && quant_mode != MOE_QUANT_W4A4) return MOE_ERR_INVALID_ARGUMENT;
   if (num_local_experts > MAX_LOCAL_EXPERTS) return MOE_ERR_UNSUPPORTED;
   GateAct act;
   s = make_act(opts->activation, opts->swiglu_alpha, opts->swiglu_beta, opts->swiglu_limit, opts->situ_beta,
@@ -375,6 +380,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
     d.w1 = w1;
     d.w1_sf = w1_sf;
     d.w1_alpha = w1_alpha;
+    d.w1_alpha_up = opts->w1_alpha_up;
     d.w2 = w2;
     d.w2_sf = w2_sf;
     d.w2_alpha = w2_alpha;
@@ -406,10 +412,10 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   if (!fused && opts->finalize_mode == MOE_FINALIZE_ATOMIC && !opts->accumulate) {
     if (launch_zero_fill(out, (size_t)M * H * 2, st) != hipSuccess) return MOE_ERR_DEVICE;
   }
-  s = moe_grouped_gemm1_act(quant_mode, x, x_sf, opts->x_row_stride, &plan, w1, w1_sf, w1_alpha, H, I,
-                            opts->activation, opts->swiglu_alpha, opts->swiglu_beta, opts->swiglu_limit,
-                            opts->situ_beta, opts->situ_linear_beta, opts->fc2_input_scale, y1, y1_sf,
-                            stream);
+  s = moe_grouped_gemm1_act(quant_mode, x, x_sf, opts->x_row_stride, &plan, w1, w1_sf, w1_alpha,
+                            opts->w1_alpha_up, H, I, opts->activation, opts->swiglu_alpha, opts->swiglu_beta,
+                            opts->swiglu_limit, opts->situ_beta, opts->situ_linear_beta, opts->fc2_input_scale,
+                            opts->per_token_scale, y1, y1_sf, stream);
   if (s != MOE_OK) return s;
   if (mark(2) != hipSuccess) return MOE_ERR_DEVICE;
   if (fused) {

@@ -62,6 +62,7 @@ struct DecArgs {
   const uint8_t* w1;
   const uint8_t* w1_sf;
   const float* w1_alpha;
+  const float* w1_alpha_up;  // NULL: w1_alpha for the up half too
   const uint8_t* w2;
   const uint8_t* w2_sf;
   const float* w2_alpha;
@@ -392,6 +393,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
     const int64_t rg = (int64_t)e * 2 * a.I + col;
     const int64_t ru = rg + a.I;
     const float al = a.w1_alpha[e];
+    const float alu = a.w1_alpha_up ? a.w1_alpha_up[e] : al;
     for (int r0 = 0; r0 < valid; r0++) {
       Chunk bg[D], bu[D];
       prefetch_pairs<D>(a.w1, a.w1_sf, rg, ru, a.H, ch, bg, bu);
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
         const float g = sum16(ag[p]);
         const float u = sum16(au[p]);
         if (ch == 0) {
-          const float y = gated_act_f32(g * al, u * al, a.act);
+          const float y = gated_act_f32(g * al, u * alu, a.act);
           a.y1[(int64_t)(slot0 + r0) * a.I + col + 16 * p] = f32_to_bf16(y);
         }
       }
@@ -691,6 +693,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   a.w1 = p.w1;
   a.w1_sf = p.w1_sf;
   a.w1_alpha = p.w1_alpha;
+  a.w1_alpha_up = p.w1_alpha_up;
   a.w2 = p.w2;
   a.w2_sf = p.w2_sf;
   a.w2_alpha = p.w2_alpha;

@@ -48,6 +48,8 @@ struct KArgs {
   const uint8_t* W;
   const uint8_t* W_sf;
   const float* alpha;
+  const float* alpha_up;  // GEMM1: the up half's scale (NULL: alpha)
+  const float* pts;       // GEMM1, W4A4: per-token input row scale (NULL: none)
   int K;                // contraction length (H for GEMM1, I for GEMM2)
   int rows_per_expert;  // 2I or H
   int I;                // GEMM1: gate/up split
@@ -321,6 +323,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
   // ---- epilogue.  Lane holds rows m*16 + 4q + i, column r16 of each tile.
   const float alpha = a.alpha[e];
   if constexpr (GEMM == 1) {
+    const float alpha_u = a.alpha_up ? a.alpha_up[e] : alpha;
     const int col = j0 + wave * 16 + r16;  // output column of y1
     float y[MT][4];
 #pragma unroll
@@ -328,7 +331,13 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         float g = acc[m][0][i] * alpha;
-        float u = acc[m][1][i] * alpha;
+        float u = acc[m][1][i] * alpha_u;
+        if (a.pts) {
+          const int row = m * 16 + 4 * q + i;
+          const float s = (row < valid) ? a.pts[row_route[row] / a.top_k] : 1.0f;
+          g = g * s;
+          u = u * s;
+        }
         // y1 is rounded once to bf16; requantisation starts from that value
         y[m][i] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
       }
@@ -473,6 +482,8 @@ hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
   a.W = p.w1;
   a.W_sf = p.w1_sf;
   a.alpha = p.w1_alpha;
+  a.alpha_up = p.w1_alpha_up;
+  a.pts = p.per_token_scale;
   a.K = p.H;
   a.rows_per_expert = 2 * p.I;
   a.I = p.I;

@@ -73,6 +73,7 @@ struct XArgs {
   const uint8_t* W;     // packed E2M1 rows, K/2 bytes
   const uint8_t* W_sf;  // E8M0, K/32 per row
   const float* alpha;
+  const float* alpha_up;  // GEMM1: the up half's scale (NULL: alpha)
   int K;
   int rows_per_expert;
   int I;
@@ -272,6 +273,7 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
   // ---- epilogue.  Lane holds slots 16m + 4q + i, column r16 of each 16-wide tile.
   const float alpha = a.alpha[e];
   if constexpr (GEMM == 1) {
+    const float alpha_u = a.alpha_up ? a.alpha_up[e] : alpha;
     // y1 block of 32 columns nb*128 + 32 wave .. : tiles 0 (gate) / 2 (up)
     // give columns +r16, tiles 1 / 3 columns 16 + r16
     const int col0 = nb * 128 + 32 * wave;
@@ -284,7 +286,7 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
 #pragma unroll
         for (int n = 0; n < 2; n++) {
           const float g = acc[m][n][i] * alpha;
-          const float u = acc[m][n + 2][i] * alpha;
+          const float u = acc[m][n + 2][i] * alpha_u;
           // y1 is rounded once to bf16; requantisation starts from that value
           y[n] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
         }
@@ -429,6 +431,7 @@ hipError_t launch_gemm1_mx(const Gemm1Params& p, hipStream_t stream) {
   a.W = p.w1;
   a.W_sf = p.w1_sf;
   a.alpha = p.w1_alpha;
+  a.alpha_up = p.w1_alpha_up;
   a.K = p.H;
   a.rows_per_expert = 2 * p.I;
   a.I = p.I;

@@ -69,6 +69,7 @@ struct WArgs {
   const uint8_t* W;
   const uint8_t* W_sf;
   const float* alpha;
+  const float* alpha_up;  // GEMM1: the up half's scale (NULL: alpha)
   int K;
   int rows_per_expert;
   int I;
@@ -274,6 +275,7 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
   // ---- epilogue.  Lane holds slots 16m + 4q + i, column r16 of each 16-wide tile.
   const float alpha = a.alpha[e];
   if constexpr (GEMM == 1) {
+    const float alpha_u = a.alpha_up ? a.alpha_up[e] : alpha;
 #pragma unroll
     for (int n = 0; n < 2; n++) {
       const int col = nb * 128 + 32 * wave + 16 * n + r16;  // y1 column
@@ -283,7 +285,7 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const float g = acc[m][n][i] * alpha;
-          const float u = acc[m][n + 2][i] * alpha;
+          const float u = acc[m][n + 2][i] * alpha_u;
           // y1 is rounded once to bf16; requantisation starts from that value
           y[m][i] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
         }
@@ -412,6 +414,7 @@ hipError_t launch_gemm1_wide(const Gemm1Params& p, hipStream_t stream) {
   a.W = p.w1;
   a.W_sf = p.w1_sf;
   a.alpha = p.w1_alpha;
+  a.alpha_up = p.w1_alpha_up;
   a.K = p.H;
   a.rows_per_expert = 2 * p.I;
   a.I = p.I;

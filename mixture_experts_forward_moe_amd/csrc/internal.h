@@ -27,9 +27,11 @@ struct Gemm1Params {
   const uint8_t* w1;
   const uint8_t* w1_sf;
   const float* w1_alpha;
+  const float* w1_alpha_up;      // NULL: w1_alpha for the up half too
   int H, I;
   GateAct act;
   const float* fc2_input_scale;
+  const float* per_token_scale;  // W4A4 only; NULL: none
   void* y1;
   uint8_t* y1_sf;
 };
@@ -76,6 +78,7 @@ struct DecodeParams {
   int64_t x_row_stride;  // elements
   const uint8_t *w1, *w1_sf;
   const float* w1_alpha;
+  const float* w1_alpha_up;  // NULL: w1_alpha for the up half too
   const uint8_t *w2, *w2_sf;
   const float* w2_alpha;
   int H, I;

@@ -38,6 +38,7 @@ struct StreamArgs {
   const uint8_t* W;
   const uint8_t* W_sf;
   const float* alpha;
+  const float* alpha_up;  // GEMM1: the up half's scale (NULL: alpha)
   int K;
   int rows_per_expert;
   int I;
@@ -160,11 +161,12 @@ __global__ __launch_bounds__(ST_THREADS) void gemm1_stream_kernel(const StreamAr
         au += red[w][1][lane];
       }
       const float al = a.alpha[e];
+      const float alu = a.alpha_up ? a.alpha_up[e] : al;
       const int col = 16 * g + c;
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int row = 4 * q + i;
-        const float y = gated_act_f32(ag[i] * al, au[i] * al, a.act);
+        const float y = gated_act_f32(ag[i] * al, au[i] * alu, a.act);
         if (row < valid) a.Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(y);
       }
     }
@@ -264,6 +266,7 @@ hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream) {
   a.W = p.w1;
   a.W_sf = p.w1_sf;
   a.alpha = p.w1_alpha;
+  a.alpha_up = p.w1_alpha_up;
   a.K = p.H;
   a.rows_per_expert = 2 * p.I;
   a.I = p.I;

@@ -102,8 +102,8 @@ def test_activation_argument_checks():
     L = moe.lib()
     p = ctypes.byref(_plan())
     F = FAKE
-    g = lambda act, a=1.0, b=0.0, lim=moe.FLT_MAX, sb=0.0, slb=0.0: L.moe_grouped_gemm1_act(
-        0, F, None, 0, p, F, F, F, 256, 512, act, a, b, lim, sb, slb, None, F, None, None)
+    g = lambda act, a=1.0, b=0.0, lim=moe.FLT_MAX, sb=0.0, slb=0.0, pts=None: L.moe_grouped_gemm1_act(
+        0, F, None, 0, p, F, F, F, None, 256, 512, act, a, b, lim, sb, slb, None, pts, F, None, None)
     assert g(moe.ACT_RELU2) == UNSUPPORTED                         # non-gated GEMM1 is not built
     assert g(7) == INVALID                                         # unknown activation
     assert g(moe.ACT_GEGLU_TANH, a=1.702) == INVALID               # GeGLU takes no SwiGLU parameters
@@ -116,6 +116,7 @@ def test_activation_argument_checks():
     assert g(moe.ACT_SWIGLU, sb=float("nan")) == INVALID
     assert g(moe.ACT_SWIGLU, sb=0.5, slb=-0.1) == INVALID
     assert g(moe.ACT_SWIGLU, lim=0.0) == INVALID
+    assert g(moe.ACT_SWIGLU, pts=F) == INVALID                     # per-token scales are W4A4 only
     # the forward checks the same rules before it enqueues anything
     o = moe.make_opts(activation=moe.ACT_RELU2)
     o.workspace = 0x10000

@@ -80,7 +80,7 @@ def test_gemm1_and_gemm2_stages(name, tile):
     y1_sf = None if s1sf is None else torch.zeros(s1sf, dtype=torch.uint8, device="cuda")
     moe.moe_grouped_gemm1_act(p.mode, d.x, d.x_sf, plan, d.w1, d.w1_sf, d.w1_alpha, p.H, p.I, y1, y1_sf,
                               p.activation, p.swiglu_alpha, p.swiglu_beta, p.swiglu_limit, p.situ_beta,
-                              p.situ_linear_beta, d.fc2)
+                              p.situ_linear_beta, d.fc2, w1_alpha_up=d.w1_alpha_up, per_token_scale=d.pts)
     torch.cuda.synchronize()
     valid = rplan.permuted_to_expanded >= 0
     gq = host(y1, dt1)[valid]
@@ -149,6 +149,46 @@ def test_atomic_finalize_and_accumulate(name):
     check_close(host(out, np.uint16), want_acc, p.mode, f"{name} atomic accumulate")
 
 
+SCALED = ["w4a16_basic", "w4a16_wide", "w4a16_stream", "w4a4_offset", "w4a4_tall", "mx_tall"]
+
+
+def scaled_problem(name):
+    """A copy of a case with its own up-half scales, per-token scales (W4A4)
+    and a routed_scaling_factor other than 1."""
+    import copy
+    p = copy.copy(problem(name))
+    rng = np.random.default_rng(70)
+    p.w1_alpha_up = (p.w1_alpha * rng.uniform(0.5, 2.0, p.w1_alpha.shape)).astype(np.float32)
+    if p.mode == oracle.W4A4:
+        p.per_token_scale = rng.uniform(0.25, 4.0, p.M).astype(np.float32)
+        oracle.set_fc2_input_scale(p, oracle.fc2_input_scale(p))   # calibrated on the scaled FC1 output
+    p.routed_scaling_factor = 1.75
+    return p
+
+
+@pytest.mark.parametrize("name", SCALED)
+@pytest.mark.parametrize("tile", [0, 16, 128])
+def test_scales_and_routed_scaling(name, tile):
+    """The up half's own per-expert scale, the W4A4 per-token input row scale
+    and routed_scaling_factor != 1 through every GEMM1 kernel and both
+    finalize modes."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, check_close, host, say
+    p = scaled_problem(name)
+    say(f"scales {name} tile={tile}")
+    d = DeviceProblem(p)
+    want = oracle.forward_tokens(p, np.arange(p.M))
+    out = d.forward(tile=tile)
+    torch.cuda.synchronize()
+    check_close(host(out, np.uint16), want, p.mode, f"{name} scaled")
+    out = torch.full((p.M, p.H), 0x3f80, dtype=torch.int16, device="cuda")
+    d.forward(out=out, tile=tile, finalize_mode=moe.FINALIZE_ATOMIC)
+    torch.cuda.synchronize()
+    check_close(host(out, np.uint16), want, p.mode, f"{name} scaled atomic")
+
+
 def test_row_strided_x():
     import torch
 
@@ -184,6 +224,12 @@ def decode_case(case):
     elif case == "one_token":
         wl = synth.small_workload(oracle.W4A16, 1, 2048, 512, 16, 16, 4, 53)
         raw = synth.make_raw(wl)
+    elif case == "scaled":
+        wl = synth.small_workload(oracle.W4A16, 7, 2048, 1024, 32, 16, 4, 61, offset=4)
+        p = oracle.quantize_problem(synth.make_raw(wl))
+        p.w1_alpha_up = (p.w1_alpha * np.float32(1.5)).astype(np.float32)
+        p.routed_scaling_factor = 2.5
+        return p
     elif case == "geglu":
         wl = synth.small_workload(oracle.W4A16, 9, 2048, 1536, 64, 16, 6, 59, offset=8,
                                   activation=oracle.ACT_GEGLU_TANH)
@@ -198,7 +244,8 @@ def decode_case(case):
     return oracle.quantize_problem(raw)
 
 
-@pytest.mark.parametrize("case", ["no_local_routes", "hot_experts", "one_token", "offset_swiglu", "geglu", "situ"])
+@pytest.mark.parametrize("case", ["no_local_routes", "hot_experts", "one_token", "offset_swiglu", "geglu", "situ",
+                                  "scaled"])
 def test_decode_path_edge_cases(case):
     """Decode-sized batches (tile 16) through the single-launch path: no
     local route at all, experts with several tiles and a ragged last tile,
