@@ -47,6 +47,7 @@ class _Moe(ctypes.Structure):
         ("fc2_input_scale", ctypes.c_float), ("routed_scaling_factor", ctypes.c_float),
         ("activation", ctypes.c_int), ("situ_beta", ctypes.c_float), ("situ_linear_beta", ctypes.c_float),
         ("w1_alpha_up", ctypes.c_void_p), ("per_token_scale", ctypes.c_void_p),
+        ("fc1_bias", ctypes.c_void_p), ("fc2_bias", ctypes.c_void_p),
     ]
 
 
@@ -267,6 +268,8 @@ class Problem:
     situ_linear_beta: float = 0.0
     w1_alpha_up: np.ndarray | None = None      # fp32 [E_l]: the up half's own scale (None: w1_alpha)
     per_token_scale: np.ndarray | None = None  # fp32 [M], W4A4: GEMM1 input row scale
+    fc1_bias: np.ndarray | None = None         # fp32 [E_l, 2I]: GEMM1 bias (gate rows, then up rows)
+    fc2_bias: np.ndarray | None = None         # fp32 [E_l, H]: GEMM2 bias
 
     def struct(self) -> _Moe:
         s = _Moe()
@@ -274,7 +277,7 @@ class Problem:
         s.top_k, s.num_experts, s.num_local_experts = self.top_k, self.num_experts, self.num_local_experts
         s.local_expert_offset = self.local_expert_offset
         for name in ("x", "x_sf", "topk_ids", "topk_weights", "w1", "w1_sf", "w1_alpha", "w2", "w2_sf", "w2_alpha",
-                     "w1_alpha_up", "per_token_scale"):
+                     "w1_alpha_up", "per_token_scale", "fc1_bias", "fc2_bias"):
             a = getattr(self, name)
             if a is not None:
                 assert a.flags["C_CONTIGUOUS"], name

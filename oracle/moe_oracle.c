@@ -375,6 +375,8 @@ typedef struct {
   float situ_linear_beta; /* > 0: SiTU tanh clamp of the up branch; 0 = unset */
   const float* w1_alpha_up;     /* NULL, or fp32 [E_l]: the up half's own scale */
   const float* per_token_scale; /* NULL, or fp32 [M] (W4A4): GEMM1 input row scale */
+  const float* fc1_bias;        /* NULL, or fp32 [E_l, 2I]: GEMM1 bias, gate then up */
+  const float* fc2_bias;        /* NULL, or fp32 [E_l, H]: GEMM2 bias */
 } orc_moe_t;
 
 static int sf_block(int mode) { return mode == ORC_MXFP8_MXFP4 ? 32 : 16; }
@@ -489,7 +491,7 @@ static float scale_acc(double acc, float alpha) {
  * output1_scale_scalar), then times the token's per_token_scale when given
  * ("flashinfer.fused_moe.cute_dsl_fused_moe", Parameters per_token_scale):
  * separate fp32 multiplies in that order. */
-static void gate_up(const orc_moe_t* p, int le, int64_t t, double G, double U, float* g, float* u) {
+static void gate_up(const orc_moe_t* p, int le, int64_t t, int j, double G, double U, float* g, float* u) {
   float gv = scale_acc(G, p->w1_alpha[le]);
   float uv = scale_acc(U, p->w1_alpha_up ? p->w1_alpha_up[le] : p->w1_alpha[le]);
   if (p->per_token_scale) {
@@ -497,8 +499,23 @@ static void gate_up(const orc_moe_t* p, int le, int64_t t, double G, double U, f
     gv = gv * s;
     uv = uv * s;
   }
+  if (p->fc1_bias) {
+    const float* b = p->fc1_bias + (int64_t)le * 2 * p->I;
+    gv = gv + b[j];
+    uv = uv + b[p->I + j];
+  }
   *g = gv;
   *u = uv;
+}
+
+/* GEMM2 output of column c through local expert le before its bf16
+ * rounding: the fp32 accumulator times w2_alpha, plus the expert's fc2 bias
+ * when given ("flashinfer.fused_moe.cutlass_fused_moe", Parameters
+ * fc1_expert_biases / fc2_expert_biases: per-expert GEMM biases). */
+static float gemm2_value(const orc_moe_t* p, int le, int c, double acc) {
+  float v = scale_acc(acc, p->w2_alpha[le]);
+  if (p->fc2_bias) v = v + p->fc2_bias[(int64_t)le * p->H + c];
+  return v;
 }
 
 /* FC1 output of one row: y1 (bf16, rounded once), then the GEMM2 input as
@@ -511,7 +528,7 @@ static void swiglu_row_and_requant(const orc_moe_t* p, int le, int64_t t, const 
   float* y = (float*)malloc((size_t)I * sizeof(float));
   for (int j = 0; j < I; j++) {
     float g, u;
-    gate_up(p, le, t, G[j], U[j], &g, &u);
+    gate_up(p, le, t, j, G[j], U[j], &g, &u);
     uint16_t b = orc_bf16_round(gated_act(p, g, u));
     if (y1_bf16) y1_bf16[j] = b;
     y[j] = orc_bf16_value(b);
@@ -569,7 +586,7 @@ void orc_gemm1_route(const orc_moe_t* p, int64_t t, int le, uint16_t* y1_bf16, u
   free(U);
 }
 
-/* GEMM2 of one route: y2[c] = bf16(fp32(sum_i a2[i] * w2[c][i]) * w2_alpha). */
+/* GEMM2 of one route: y2[c] = bf16(fp32(sum_i a2[i] * w2[c][i]) * w2_alpha [+ fc2_bias]). */
 void orc_gemm2_route(const orc_moe_t* p, int le, const double* a2, uint16_t* y2) {
   int H = p->H, I = p->I;
 #pragma omp parallel
@@ -580,7 +597,7 @@ void orc_gemm2_route(const orc_moe_t* p, int le, const double* a2, uint16_t* y2)
       const uint8_t* sf;
       const uint8_t* q = w2_row(p, le, c, &sf);
       dequant_w_row(p->mode, q, sf, I, w);
-      y2[c] = orc_bf16_round(scale_acc(dot(a2, w, I), p->w2_alpha[le]));
+      y2[c] = orc_bf16_round(gemm2_value(p, le, c, dot(a2, w, I)));
     }
     free(w);
   }
@@ -710,7 +727,7 @@ void orc_forward_plan(const orc_moe_t* p, int tile, int32_t* e2p, int32_t* p2e,
         }
         swiglu_row_and_requant(p, le, t, G, U, yb, yq, ys, a2);
         for (int c = 0; c < H; c++)
-          y2[slot * H + c] = orc_bf16_round(scale_acc(dot(a2, wd2 + (int64_t)c * I, I), p->w2_alpha[le]));
+          y2[slot * H + c] = orc_bf16_round(gemm2_value(p, le, c, dot(a2, wd2 + (int64_t)c * I, I)));
       }
       free(a);
       free(G);
@@ -747,7 +764,7 @@ float orc_fc2_input_scale(const orc_moe_t* p) {
         dequant_x_row(p, r / k, a);
         for (int n = 0; n < I; n++) {
           float g, u;
-          gate_up(p, le, r / k, dot(a, wd1 + (int64_t)n * H, H), dot(a, wd1 + (int64_t)(I + n) * H, H), &g, &u);
+          gate_up(p, le, r / k, n, dot(a, wd1 + (int64_t)n * H, H), dot(a, wd1 + (int64_t)(I + n) * H, H), &g, &u);
           uint16_t b = orc_bf16_round(gated_act(p, g, u));
           float v = fabsf(orc_bf16_value(b));
           if (v > local) local = v;

@@ -161,6 +161,9 @@ def forward_tokens(p, tokens):
                 pts = np.float32(p.per_token_scale[t])
                 g = (g * pts).astype(np.float32)
                 u = (u * pts).astype(np.float32)
+            if getattr(p, "fc1_bias", None) is not None:
+                g = (g + p.fc1_bias[le, :I]).astype(np.float32)
+                u = (u + p.fc1_bias[le, I:]).astype(np.float32)
             y1 = bf16_vals(to_bf16_bits(gated_act(p, g, u)))
             if p.mode == W4A16:
                 a2 = y1
@@ -169,7 +172,10 @@ def forward_tokens(p, tokens):
             else:
                 a2 = quant_mxfp8(y1.astype(np.float32))
             Y = W2d @ a2
-            y2 = bf16_vals(to_bf16_bits((Y.astype(np.float32) * np.float32(p.w2_alpha[le])).astype(np.float32)))
+            Y2 = (Y.astype(np.float32) * np.float32(p.w2_alpha[le])).astype(np.float32)
+            if getattr(p, "fc2_bias", None) is not None:
+                Y2 = (Y2 + p.fc2_bias[le]).astype(np.float32)
+            y2 = bf16_vals(to_bf16_bits(Y2))
             wf = np.float32(np.float32(p.topk_weights[t, j]) * np.float32(p.routed_scaling_factor))
             acc = (acc + (wf * y2.astype(np.float32)).astype(np.float32)).astype(np.float32)
         out[i] = to_bf16_bits(acc.astype(np.float64))

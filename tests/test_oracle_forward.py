@@ -194,6 +194,46 @@ def test_power_of_two_up_scale_scales_y1_exactly():
     assert np.array_equal(synth.bf16_to_f32(y1[valid]) * 2, synth.bf16_to_f32(y1b[valid]))
 
 
+def _biased_problem(mode, seed):
+    p = _problem(mode, M=9, H=64, I=64, E=8, El=6, k=3, seed=seed, offset=1)
+    rng = np.random.default_rng(seed)
+    p.fc1_bias = rng.normal(0.0, 0.05, (p.num_local_experts, 2 * p.I)).astype(np.float32)
+    p.fc2_bias = rng.normal(0.0, 0.05, (p.num_local_experts, p.H)).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("mode", [oracle.W4A16, oracle.W4A4, oracle.MXFP8_MXFP4])
+def test_fc_biases_against_library_reference(mode):
+    p = _biased_problem(mode, 71 + mode)
+    if mode == oracle.W4A4:
+        oracle.set_fc2_input_scale(p, oracle.fc2_input_scale(p))
+    tokens = np.arange(p.M)
+    got = oracle.forward_tokens(p, tokens)
+    _close_bf16(got, ref.forward_tokens(p, tokens))
+    _, _, _, _, out = oracle.forward_plan(p, 4)
+    assert np.array_equal(out, got)
+
+
+def test_fc_biases_closed_forms():
+    p = _biased_problem(oracle.W4A16, 74)
+    plain = oracle.forward_tokens(_problem(oracle.W4A16, M=9, H=64, I=64, E=8, El=6, k=3, seed=74, offset=1),
+                                  np.arange(p.M))
+    zero = _biased_problem(oracle.W4A16, 74)
+    zero.fc1_bias = np.zeros_like(zero.fc1_bias)
+    zero.fc2_bias = np.zeros_like(zero.fc2_bias)
+    assert np.array_equal(oracle.forward_tokens(zero, np.arange(p.M)), plain)   # zero biases are no biases
+    # all-zero weight codes: the accumulators vanish, so y1 = bf16(silu(b_gate) * b_up) and y2 = bf16(b2)
+    p.w1 = np.zeros_like(p.w1)
+    p.w2 = np.zeros_like(p.w2)
+    plan, y1, _, y2, _ = oracle.forward_plan(p, 4)
+    for slot in np.nonzero(plan.permuted_to_expanded >= 0)[0]:
+        le = int(p.topk_ids.reshape(-1)[plan.permuted_to_expanded[slot]]) - p.local_expert_offset
+        bg, bu = p.fc1_bias[le, :p.I], p.fc1_bias[le, p.I:]
+        want1 = ref.to_bf16_bits(np.array([oracle.swiglu(float(g), float(u)) for g, u in zip(bg, bu)]))
+        assert np.array_equal(y1[slot], want1)
+        assert np.array_equal(y2[slot], ref.to_bf16_bits(p.fc2_bias[le].astype(np.float64)))
+
+
 def test_power_of_two_w2_alpha_scales_y2_exactly():
     p = _problem(oracle.W4A16, M=8, H=64, I=32, E=4, El=4, k=2, seed=32)
     _, _, _, y2, _ = oracle.forward_plan(p, 8)
