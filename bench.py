@@ -123,11 +123,16 @@ def _opts(moe, wl, ws, tile, fc2=None, **kw):
 
 def _scale_kw(g, scaled: bool):
     """Options of the scaled variant: the up half with its own per-expert
-    scale (1.5x the gate's) and routed_scaling_factor 1.75."""
+    scale (1.5x the gate's), FC1 and FC2 biases (0.01) and
+    routed_scaling_factor 1.75."""
     if not scaled:
         return {}
+    import torch
     w1a = g.copies[0][5]
-    return dict(w1_alpha_up=(w1a * 1.5).contiguous(), routed_scaling_factor=1.75)
+    E, H, I = g.wl.num_local_experts, g.wl.H, g.wl.I
+    return dict(w1_alpha_up=(w1a * 1.5).contiguous(), routed_scaling_factor=1.75,
+                fc1_bias=torch.full((E, 2 * I), 0.01, dtype=torch.float32, device="cuda"),
+                fc2_bias=torch.full((E, H), 0.01, dtype=torch.float32, device="cuda"))
 
 
 def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False):
@@ -428,8 +433,8 @@ def main():
                           "weight_bytes": wb, "weights_hbm_frac": wb / (r3["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "note": note}
     if not args.no_secondary:
-        # the other FC1 epilogues on the decode and prefill workloads (GeGLU-tanh, SiTU, and SwiGLU with
-        # the up half's own scale and routed_scaling_factor 1.75): the decode forward in graph replay
+        # the other GEMM epilogues on the decode and prefill workloads (GeGLU-tanh, SiTU, and SwiGLU with
+        # the up half's own scale, FC1 / FC2 biases and routed_scaling_factor 1.75): the decode forward in graph replay
         # (same roofline unit as the headline) and the prefill GEMM1 with per-kernel events
         import dataclasses
         acts = {}
@@ -445,7 +450,8 @@ def main():
             rp = time_phases(wp, 10, 3, args.copies, scaled=scaled)
             g1 = 4.0 * wp.H * wp.I * rp["local_routes"] / (rp["phase_ms"]["gemm1"] * 1e-3) / 1e12
             if scaled:
-                kw = {"w1_alpha_up": "1.5 x w1_alpha", "routed_scaling_factor": 1.75}
+                kw = {"w1_alpha_up": "1.5 x w1_alpha", "fc1_bias": 0.01, "fc2_bias": 0.01,
+                      "routed_scaling_factor": 1.75}
             acts[name] = {"params": kw, "decode_ms_per_forward": rd["gpu_ms_per_step"], "decode_hbm_frac": fd / HBM_PEAK_GBS,
                           "prefill_gemm1_ms": rp["phase_ms"]["gemm1"], "prefill_gemm1_mfma_frac": g1 / BF16_PEAK_TFLOPS}
         acts["swiglu"] = {"decode_ms_per_forward": f_ms, "decode_hbm_frac": f_gbs / HBM_PEAK_GBS,

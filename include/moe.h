@@ -185,6 +185,9 @@ typedef enum moe_activation {
  *     per_token_scale), applied after the expert scale:
  *     g = fp32(fp32(acc_g) * w1_alpha[e]) * per_token_scale[t], likewise u.
  *     NULL: none.  Non-NULL outside W4A4: MOE_ERR_INVALID_ARGUMENT.
+ *   fc1_bias: device fp32 [E_l, 2I] (gate rows, then up rows), added to g and
+ *     u after the scales, before the activation ("flashinfer.fused_moe.
+ *     cutlass_fused_moe", Parameters fc1_expert_biases).  NULL: none.
  * The activations (same Parameters of cute_dsl_fused_moe):
  *   MOE_ACT_SWIGLU, situ_beta == 0: the SwiGLU above.
  *   MOE_ACT_SWIGLU, situ_beta  > 0: SiTU,
@@ -202,8 +205,8 @@ moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const u
                                    const uint8_t* w1_sf, const float* w1_alpha, const float* w1_alpha_up, int H,
                                    int I, int activation, float swiglu_alpha, float swiglu_beta,
                                    float swiglu_limit, float situ_beta, float situ_linear_beta,
-                                   const float* fc2_input_scale, const float* per_token_scale, void* y1,
-                                   uint8_t* y1_sf, moe_stream_t stream);
+                                   const float* fc2_input_scale, const float* per_token_scale,
+                                   const float* fc1_bias, void* y1, uint8_t* y1_sf, moe_stream_t stream);
 
 /* moe_grouped_gemm2: for every valid slot s of local expert e, multiply the
  * stored FC1 output (decoded as moe_grouped_gemm1_swiglu wrote it; in W4A4
@@ -222,6 +225,17 @@ moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint
                                const moe_plan_t* plan, const uint8_t* w2, const uint8_t* w2_sf,
                                const float* w2_alpha, int H, int I, uint16_t* y2, const float* topk_weights,
                                float routed_scaling_factor, uint16_t* out, moe_stream_t stream);
+
+/* moe_grouped_gemm2_bias: moe_grouped_gemm2 with a per-expert GEMM2 bias
+ * fc2_bias, device fp32 [E_l, H], added to alpha2 * result before y2's bf16
+ * rounding (and before the routing weight in atomic mode)
+ * ("flashinfer.fused_moe.cutlass_fused_moe", Parameters fc2_expert_biases;
+ * the page calls it the GEMM1 bias, read as GEMM2's).  NULL: none. */
+moe_status_t moe_grouped_gemm2_bias(moe_quant_mode_t mode, const void* y1, const uint8_t* y1_sf,
+                                    const moe_plan_t* plan, const uint8_t* w2, const uint8_t* w2_sf,
+                                    const float* w2_alpha, const float* fc2_bias, int H, int I, uint16_t* y2,
+                                    const float* topk_weights, float routed_scaling_factor, uint16_t* out,
+                                    moe_stream_t stream);
 
 /* moe_finalize: deterministic weighted top-k reduction
  * ("flashinfer.fused_moe.alphamoe_nvfp4_routed_moe", summary and
@@ -261,6 +275,8 @@ typedef struct moe_opts {
   float situ_linear_beta;        /* default 0 (no up-branch clamp) */
   const float* w1_alpha_up;      /* device fp32 [E_l]: the up half's scale; NULL = w1_alpha */
   const float* per_token_scale;  /* device fp32 [M], W4A4 only: GEMM1 input row scale; NULL = none */
+  const float* fc1_bias;         /* device fp32 [E_l, 2I]: GEMM1 bias (moe_grouped_gemm1_act); NULL = none */
+  const float* fc2_bias;         /* device fp32 [E_l, H]: GEMM2 bias (moe_grouped_gemm2_bias); NULL = none */
 } moe_opts_t;
 
 #define MOE_NUM_PHASE_EVENTS 5

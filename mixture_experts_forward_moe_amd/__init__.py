@@ -23,7 +23,7 @@ ACT_SWIGLU, ACT_GEGLU_TANH, ACT_RELU2 = 0, 1, 2   # moe_activation_t (SiTU: ACT_
 
 EXPORTS = [
     "moe_status_string", "moe_route_slots", "moe_plan_workspace_size", "moe_plan_init", "moe_sort",
-    "moe_grouped_gemm1_swiglu", "moe_grouped_gemm1_act", "moe_grouped_gemm2", "moe_finalize", "moe_opts_init", "moe_default_tile",
+    "moe_grouped_gemm1_swiglu", "moe_grouped_gemm1_act", "moe_grouped_gemm2", "moe_grouped_gemm2_bias", "moe_finalize", "moe_opts_init", "moe_default_tile",
     "moe_workspace_size", "moe_forward", "moe_nvfp4_global_scale", "moe_quantize_nvfp4", "moe_quantize_mx",
 ]
 
@@ -54,6 +54,7 @@ class Opts(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t), ("phase_events", ctypes.c_void_p),
         ("activation", ctypes.c_int), ("situ_beta", ctypes.c_float), ("situ_linear_beta", ctypes.c_float),
         ("w1_alpha_up", ctypes.c_void_p), ("per_token_scale", ctypes.c_void_p),
+        ("fc1_bias", ctypes.c_void_p), ("fc2_bias", ctypes.c_void_p),
     ]
 
 
@@ -75,7 +76,8 @@ def lib() -> ctypes.CDLL:
             "moe_plan_init": ([P, P, SZ, I, I, I, I], I),
             "moe_sort": ([P, I, I, I, I, I, I, P, P], I),
             "moe_grouped_gemm1_swiglu": ([I, P, P, I64, P, P, P, P, I, I, F, F, F, P, P, P, P], I),
-            "moe_grouped_gemm1_act": ([I, P, P, I64, P, P, P, P, P, I, I, I, F, F, F, F, F, P, P, P, P, P], I),
+            "moe_grouped_gemm1_act": ([I, P, P, I64, P, P, P, P, P, I, I, I, F, F, F, F, F, P, P, P, P, P, P], I),
+            "moe_grouped_gemm2_bias": ([I, P, P, P, P, P, P, P, I, I, P, P, F, P, P], I),
             "moe_grouped_gemm2": ([I, P, P, P, P, P, P, I, I, P, P, F, P, P], I),
             "moe_finalize": ([P, P, P, I, F, I, P, P], I),
             "moe_opts_init": ([P], None),
@@ -208,19 +210,26 @@ def moe_grouped_gemm1_swiglu(mode, x, x_sf, plan: MoePlan, w1, w1_sf, w1_alpha, 
 def moe_grouped_gemm1_act(mode, x, x_sf, plan: MoePlan, w1, w1_sf, w1_alpha, H, I, y1, y1_sf=None,
                           activation=ACT_SWIGLU, swiglu_alpha=1.0, swiglu_beta=0.0, swiglu_limit=FLT_MAX,
                           situ_beta=0.0, situ_linear_beta=0.0, fc2_input_scale=None, x_row_stride=0, stream=None,
-                          w1_alpha_up=None, per_token_scale=None):
+                          w1_alpha_up=None, per_token_scale=None, fc1_bias=None):
     _check(lib().moe_grouped_gemm1_act(mode, _ptr(x), _ptr(x_sf), x_row_stride, ctypes.byref(plan.c), _ptr(w1),
                                        _ptr(w1_sf), _ptr(w1_alpha), _ptr(w1_alpha_up), H, I, activation,
                                        swiglu_alpha, swiglu_beta, swiglu_limit, situ_beta, situ_linear_beta,
-                                       _ptr(fc2_input_scale), _ptr(per_token_scale), _ptr(y1), _ptr(y1_sf),
+                                       _ptr(fc2_input_scale), _ptr(per_token_scale), _ptr(fc1_bias), _ptr(y1),
+                                       _ptr(y1_sf),
                                        _stream(stream)), "moe_grouped_gemm1_act")
 
 
 def moe_grouped_gemm2(mode, y1, y1_sf, plan: MoePlan, w2, w2_sf, w2_alpha, H, I, y2=None, topk_weights=None,
-                      routed_scaling_factor=1.0, out=None, stream=None):
-    _check(lib().moe_grouped_gemm2(mode, _ptr(y1), _ptr(y1_sf), ctypes.byref(plan.c), _ptr(w2), _ptr(w2_sf),
-                                   _ptr(w2_alpha), H, I, _ptr(y2), _ptr(topk_weights), routed_scaling_factor,
-                                   _ptr(out), _stream(stream)), "moe_grouped_gemm2")
+                      routed_scaling_factor=1.0, out=None, stream=None, fc2_bias=None):
+    if fc2_bias is None:
+        _check(lib().moe_grouped_gemm2(mode, _ptr(y1), _ptr(y1_sf), ctypes.byref(plan.c), _ptr(w2), _ptr(w2_sf),
+                                       _ptr(w2_alpha), H, I, _ptr(y2), _ptr(topk_weights), routed_scaling_factor,
+                                       _ptr(out), _stream(stream)), "moe_grouped_gemm2")
+    else:
+        _check(lib().moe_grouped_gemm2_bias(mode, _ptr(y1), _ptr(y1_sf), ctypes.byref(plan.c), _ptr(w2),
+                                            _ptr(w2_sf), _ptr(w2_alpha), _ptr(fc2_bias), H, I, _ptr(y2),
+                                            _ptr(topk_weights), routed_scaling_factor, _ptr(out), _stream(stream)),
+               "moe_grouped_gemm2_bias")
 
 
 def moe_finalize(y2, plan: MoePlan, topk_weights, H, out, routed_scaling_factor=1.0, accumulate=False, stream=None):
@@ -231,13 +240,16 @@ def moe_finalize(y2, plan: MoePlan, topk_weights, H, out, routed_scaling_factor=
 def make_opts(workspace=None, swiglu_alpha=1.0, swiglu_beta=0.0, swiglu_limit=FLT_MAX, fc2_input_scale=None,
               routed_scaling_factor=1.0, accumulate=False, finalize_mode=FINALIZE_DETERMINISTIC,
               route_order=ROUTE_ORDER_AUTO, tile=0, x_row_stride=0, phase_events=None, activation=ACT_SWIGLU,
-              situ_beta=0.0, situ_linear_beta=0.0, w1_alpha_up=None, per_token_scale=None) -> Opts:
+              situ_beta=0.0, situ_linear_beta=0.0, w1_alpha_up=None, per_token_scale=None, fc1_bias=None,
+              fc2_bias=None) -> Opts:
     o = Opts()
     lib().moe_opts_init(ctypes.byref(o))
     o.swiglu_alpha, o.swiglu_beta, o.swiglu_limit = swiglu_alpha, swiglu_beta, swiglu_limit
     o.activation, o.situ_beta, o.situ_linear_beta = activation, situ_beta, situ_linear_beta
     o.w1_alpha_up = None if w1_alpha_up is None else w1_alpha_up.data_ptr()
     o.per_token_scale = None if per_token_scale is None else per_token_scale.data_ptr()
+    o.fc1_bias = None if fc1_bias is None else fc1_bias.data_ptr()
+    o.fc2_bias = None if fc2_bias is None else fc2_bias.data_ptr()
     o.fc2_input_scale = None if fc2_input_scale is None else fc2_input_scale.data_ptr()
     o.routed_scaling_factor = routed_scaling_factor
     o.accumulate = int(bool(accumulate))

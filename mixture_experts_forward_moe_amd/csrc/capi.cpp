@@ -177,8 +177,8 @@ moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const u
                                    const uint8_t* w1_sf, const float* w1_alpha, const float* w1_alpha_up, int H,
                                    int I, int activation, float swiglu_alpha, float swiglu_beta,
                                    float swiglu_limit, float situ_beta, float situ_linear_beta,
-                                   const float* fc2_input_scale, const float* per_token_scale, void* y1,
-                                   uint8_t* y1_sf, moe_stream_t stream) {
+                                   const float* fc2_input_scale, const float* per_token_scale,
+                                   const float* fc1_bias, void* y1, uint8_t* y1_sf, moe_stream_t stream) {
   if (!mode_ok(mode) || !plan_ok(plan)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status_t s = shape_check(H, I, mode);
   if (s != MOE_OK) return s;
@@ -192,7 +192,7 @@ moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const u
   if (x_row_stride != 0 && x_row_stride < row_units) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t stride = x_row_stride ? x_row_stride : row_units;
   if ((stride * (mode == MOE_QUANT_W4A16 ? 2 : 1)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
-  Gemm1Params p;
+  Gemm1Params p = {};
   s = make_act(activation, swiglu_alpha, swiglu_beta, swiglu_limit, situ_beta, situ_linear_beta, &p.act);
   if (s != MOE_OK) return s;
   p.mode = mode;
@@ -208,6 +208,7 @@ moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const u
   p.I = I;
   p.fc2_input_scale = fc2_input_scale;
   p.per_token_scale = per_token_scale;
+  p.fc1_bias = fc1_bias;
   p.y1 = y1;
   p.y1_sf = y1_sf;
   if (plan->M == 0) return MOE_OK;
@@ -222,13 +223,14 @@ moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, cons
                                       moe_stream_t stream) {
   return moe_grouped_gemm1_act(mode, x, x_sf, x_row_stride, plan, w1, w1_sf, w1_alpha, NULL, H, I,
                                MOE_ACT_SWIGLU, swiglu_alpha, swiglu_beta, swiglu_limit, 0.0f, 0.0f,
-                               fc2_input_scale, NULL, y1, y1_sf, stream);
+                               fc2_input_scale, NULL, NULL, y1, y1_sf, stream);
 }
 
-moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint8_t* y1_sf,
-                               const moe_plan_t* plan, const uint8_t* w2, const uint8_t* w2_sf,
-                               const float* w2_alpha, int H, int I, uint16_t* y2, const float* topk_weights,
-                               float routed_scaling_factor, uint16_t* out, moe_stream_t stream) {
+moe_status_t moe_grouped_gemm2_bias(moe_quant_mode_t mode, const void* y1, const uint8_t* y1_sf,
+                                    const moe_plan_t* plan, const uint8_t* w2, const uint8_t* w2_sf,
+                                    const float* w2_alpha, const float* fc2_bias, int H, int I, uint16_t* y2,
+                                    const float* topk_weights, float routed_scaling_factor, uint16_t* out,
+                                    moe_stream_t stream) {
   if (!mode_ok(mode) || !plan_ok(plan)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status_t s = shape_check(H, I, mode);
   if (s != MOE_OK) return s;
@@ -236,7 +238,7 @@ moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint
   if ((mode == MOE_QUANT_W4A16) != (y1_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
   if ((y2 == NULL) == (out == NULL)) return MOE_ERR_INVALID_ARGUMENT;  // exactly one finalize mode
   if (out && !topk_weights) return MOE_ERR_INVALID_ARGUMENT;
-  Gemm2Params p;
+  Gemm2Params p = {};
   p.mode = mode;
   p.y1 = y1;
   p.y1_sf = y1_sf;
@@ -244,6 +246,7 @@ moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint
   p.w2 = w2;
   p.w2_sf = w2_sf;
   p.w2_alpha = w2_alpha;
+  p.fc2_bias = fc2_bias;
   p.H = H;
   p.I = I;
   p.y2 = y2;
@@ -252,6 +255,14 @@ moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint
   p.out = out;
   if (plan->M == 0) return MOE_OK;
   return dev(launch_gemm2(p, (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint8_t* y1_sf,
+                               const moe_plan_t* plan, const uint8_t* w2, const uint8_t* w2_sf,
+                               const float* w2_alpha, int H, int I, uint16_t* y2, const float* topk_weights,
+                               float routed_scaling_factor, uint16_t* out, moe_stream_t stream) {
+  return moe_grouped_gemm2_bias(mode, y1, y1_sf, plan, w2, w2_sf, w2_alpha, NULL, H, I, y2, topk_weights,
+                                routed_scaling_factor, out, stream);
 }
 
 moe_status_t moe_finalize(const uint16_t* y2, const moe_plan_t* plan, const float* topk_weights, int H,
@@ -372,7 +383,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   }
   if (dec) {
     // decode-sized batch: GEMM1 (with the routing plan), then GEMM2 with the finalize
-    DecodeParams d;
+    DecodeParams d = {};
     d.topk_ids = topk_ids;
     d.local_expert_offset = local_expert_offset;
     d.x = x;
@@ -381,6 +392,8 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
     d.w1_sf = w1_sf;
     d.w1_alpha = w1_alpha;
     d.w1_alpha_up = opts->w1_alpha_up;
+    d.fc1_bias = opts->fc1_bias;
+    d.fc2_bias = opts->fc2_bias;
     d.w2 = w2;
     d.w2_sf = w2_sf;
     d.w2_alpha = w2_alpha;
@@ -415,11 +428,11 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   s = moe_grouped_gemm1_act(quant_mode, x, x_sf, opts->x_row_stride, &plan, w1, w1_sf, w1_alpha,
                             opts->w1_alpha_up, H, I, opts->activation, opts->swiglu_alpha, opts->swiglu_beta,
                             opts->swiglu_limit, opts->situ_beta, opts->situ_linear_beta, opts->fc2_input_scale,
-                            opts->per_token_scale, y1, y1_sf, stream);
+                            opts->per_token_scale, opts->fc1_bias, y1, y1_sf, stream);
   if (s != MOE_OK) return s;
   if (mark(2) != hipSuccess) return MOE_ERR_DEVICE;
   if (fused) {
-    Gemm2Params p;
+    Gemm2Params p = {};
     p.mode = quant_mode;
     p.y1 = y1;
     p.y1_sf = y1_sf;
@@ -427,6 +440,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
     p.w2 = w2;
     p.w2_sf = w2_sf;
     p.w2_alpha = w2_alpha;
+    p.fc2_bias = opts->fc2_bias;
     p.H = H;
     p.I = I;
     p.y2 = NULL;
@@ -436,15 +450,15 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
     if (launch_gemm2_stream(p, opts->accumulate, st) != hipSuccess) return MOE_ERR_DEVICE;
     if (mark(3) != hipSuccess) return MOE_ERR_DEVICE;
   } else if (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC) {
-    s = moe_grouped_gemm2(quant_mode, y1, y1_sf, &plan, w2, w2_sf, w2_alpha, H, I, y2, NULL,
-                          opts->routed_scaling_factor, NULL, stream);
+    s = moe_grouped_gemm2_bias(quant_mode, y1, y1_sf, &plan, w2, w2_sf, w2_alpha, opts->fc2_bias, H, I, y2,
+                               NULL, opts->routed_scaling_factor, NULL, stream);
     if (s != MOE_OK) return s;
     if (mark(3) != hipSuccess) return MOE_ERR_DEVICE;
     s = moe_finalize(y2, &plan, topk_weights, H, opts->routed_scaling_factor, opts->accumulate, out, stream);
     if (s != MOE_OK) return s;
   } else {
-    s = moe_grouped_gemm2(quant_mode, y1, y1_sf, &plan, w2, w2_sf, w2_alpha, H, I, NULL, topk_weights,
-                          opts->routed_scaling_factor, out, stream);
+    s = moe_grouped_gemm2_bias(quant_mode, y1, y1_sf, &plan, w2, w2_sf, w2_alpha, opts->fc2_bias, H, I, NULL,
+                               topk_weights, opts->routed_scaling_factor, out, stream);
     if (s != MOE_OK) return s;
     if (mark(3) != hipSuccess) return MOE_ERR_DEVICE;
   }

@@ -63,6 +63,8 @@ struct DecArgs {
   const uint8_t* w1_sf;
   const float* w1_alpha;
   const float* w1_alpha_up;  // NULL: w1_alpha for the up half too
+  const float* fc1_bias;     // NULL, or fp32 [El, 2I]
+  const float* fc2_bias;     // NULL, or fp32 [El, H]
   const uint8_t* w2;
   const uint8_t* w2_sf;
   const float* w2_alpha;
@@ -425,7 +427,12 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
         const float g = sum16(ag[p]);
         const float u = sum16(au[p]);
         if (ch == 0) {
-          const float y = gated_act_f32(g * al, u * alu, a.act);
+          float gs = g * al, us = u * alu;
+          if (a.fc1_bias) {
+            gs = gs + a.fc1_bias[(int64_t)e * 2 * a.I + col + 16 * p];
+            us = us + a.fc1_bias[(int64_t)e * 2 * a.I + a.I + col + 16 * p];
+          }
+          const float y = gated_act_f32(gs, us, a.act);
           a.y1[(int64_t)(slot0 + r0) * a.I + col + 16 * p] = f32_to_bf16(y);
         }
       }
@@ -650,7 +657,9 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm2_kernel(const DecArgs a)
 #pragma unroll
       for (int g = 0; g < 4; g++) {
         const float v = sum16(acc[g][0]);
-        if (ch == 0) ybuf[16 * wave + 4 * g + rr] = f32_to_bf16(v * al);
+        float y2v = v * al;
+        if (a.fc2_bias) y2v = y2v + a.fc2_bias[(int64_t)e * a.H + c0 + 16 * wave + 4 * g + rr];
+        if (ch == 0) ybuf[16 * wave + 4 * g + rr] = f32_to_bf16(y2v);
       }
       lds_barrier();
       // the row's 64 outputs: one 128-byte line from 32 lanes
@@ -694,6 +703,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   a.w1_sf = p.w1_sf;
   a.w1_alpha = p.w1_alpha;
   a.w1_alpha_up = p.w1_alpha_up;
+  a.fc1_bias = p.fc1_bias;
+  a.fc2_bias = p.fc2_bias;
   a.w2 = p.w2;
   a.w2_sf = p.w2_sf;
   a.w2_alpha = p.w2_alpha;

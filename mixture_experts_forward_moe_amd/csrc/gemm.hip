@@ -50,6 +50,7 @@ struct KArgs {
   const float* alpha;
   const float* alpha_up;  // GEMM1: the up half's scale (NULL: alpha)
   const float* pts;       // GEMM1, W4A4: per-token input row scale (NULL: none)
+  const float* bias;      // NULL, or fp32 [E, 2I] (GEMM1: gate then up) / [E, H] (GEMM2)
   int K;                // contraction length (H for GEMM1, I for GEMM2)
   int rows_per_expert;  // 2I or H
   int I;                // GEMM1: gate/up split
@@ -338,6 +339,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
           g = g * s;
           u = u * s;
         }
+        if (a.bias) {
+          g = g + a.bias[(int64_t)e * 2 * a.I + col];
+          u = u + a.bias[(int64_t)e * 2 * a.I + a.I + col];
+        }
         // y1 is rounded once to bf16; requantisation starts from that value
         y[m][i] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
       }
@@ -409,7 +414,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
 #pragma unroll
             for (int n = 0; n < 2; n++) {
               int col = n0 + wave * 32 + n * 16 + r16;
-              Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(acc[m][n][i] * alpha);
+              float v = acc[m][n][i] * alpha;
+              if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
+              Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(v);
             }
           }
         } else {
@@ -418,7 +425,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
 #pragma unroll
           for (int n = 0; n < 2; n++) {
             int col = n0 + wave * 32 + n * 16 + r16;
-            float y2 = bf16_to_f32(f32_to_bf16(acc[m][n][i] * alpha));
+            float v = acc[m][n][i] * alpha;
+            if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
+            float y2 = bf16_to_f32(f32_to_bf16(v));
             float c = __fmul_rn(wf, y2);
             float cn = __shfl_xor(c, 1);
             if (route >= 0 && (r16 & 1) == 0) {
@@ -484,6 +493,7 @@ hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
   a.alpha = p.w1_alpha;
   a.alpha_up = p.w1_alpha_up;
   a.pts = p.per_token_scale;
+  a.bias = p.fc1_bias;
   a.K = p.H;
   a.rows_per_expert = 2 * p.I;
   a.I = p.I;
@@ -511,6 +521,7 @@ hipError_t launch_gemm2(const Gemm2Params& p, hipStream_t stream) {
   a.W = p.w2;
   a.W_sf = p.w2_sf;
   a.alpha = p.w2_alpha;
+  a.bias = p.fc2_bias;
   a.K = p.I;
   a.rows_per_expert = p.H;
   a.I = p.I;

@@ -74,6 +74,7 @@ struct XArgs {
   const uint8_t* W_sf;  // E8M0, K/32 per row
   const float* alpha;
   const float* alpha_up;  // GEMM1: the up half's scale (NULL: alpha)
+  const float* bias;      // NULL, or fp32 [E, 2I] (GEMM1: gate then up) / [E, H] (GEMM2)
   int K;
   int rows_per_expert;
   int I;
@@ -285,8 +286,12 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
         float y[2];
 #pragma unroll
         for (int n = 0; n < 2; n++) {
-          const float g = acc[m][n][i] * alpha;
-          const float u = acc[m][n + 2][i] * alpha_u;
+          float g = acc[m][n][i] * alpha;
+          float u = acc[m][n + 2][i] * alpha_u;
+          if (a.bias) {
+            g = g + a.bias[(int64_t)e * 2 * a.I + col0 + 16 * n + r16];
+            u = u + a.bias[(int64_t)e * 2 * a.I + a.I + col0 + 16 * n + r16];
+          }
           // y1 is rounded once to bf16; requantisation starts from that value
           y[n] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
         }
@@ -317,7 +322,9 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
 #pragma unroll
             for (int n = 0; n < 4; n++) {
               const int col = nb * XN + 64 * wave + 16 * n + r16;
-              Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(acc[m][n][i] * alpha);
+              float v = acc[m][n][i] * alpha;
+              if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
+              Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(v);
             }
           }
         } else {
@@ -326,7 +333,9 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
 #pragma unroll
           for (int n = 0; n < 4; n++) {
             const int col = nb * XN + 64 * wave + 16 * n + r16;
-            const float y2 = bf16_to_f32(f32_to_bf16(acc[m][n][i] * alpha));
+            float v = acc[m][n][i] * alpha;
+            if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
+            const float y2 = bf16_to_f32(f32_to_bf16(v));
             const float c = __fmul_rn(wf, y2);
             const float cn = __shfl_xor(c, 1);
             if (route >= 0 && (r16 & 1) == 0) {
@@ -432,6 +441,7 @@ hipError_t launch_gemm1_mx(const Gemm1Params& p, hipStream_t stream) {
   a.W_sf = p.w1_sf;
   a.alpha = p.w1_alpha;
   a.alpha_up = p.w1_alpha_up;
+  a.bias = p.fc1_bias;
   a.K = p.H;
   a.rows_per_expert = 2 * p.I;
   a.I = p.I;
@@ -453,6 +463,7 @@ hipError_t launch_gemm2_mx(const Gemm2Params& p, hipStream_t stream) {
   a.W = p.w2;
   a.W_sf = p.w2_sf;
   a.alpha = p.w2_alpha;
+  a.bias = p.fc2_bias;
   a.K = p.I;
   a.rows_per_expert = p.H;
   a.I = p.I;

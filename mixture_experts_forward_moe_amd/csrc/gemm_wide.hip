@@ -70,6 +70,7 @@ struct WArgs {
   const uint8_t* W_sf;
   const float* alpha;
   const float* alpha_up;  // GEMM1: the up half's scale (NULL: alpha)
+  const float* bias;      // NULL, or fp32 [E, 2I] (GEMM1: gate then up) / [E, H] (GEMM2)
   int K;
   int rows_per_expert;
   int I;
@@ -284,8 +285,12 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
       for (int m = 0; m < MTV; m++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const float g = acc[m][n][i] * alpha;
-          const float u = acc[m][n + 2][i] * alpha_u;
+          float g = acc[m][n][i] * alpha;
+          float u = acc[m][n + 2][i] * alpha_u;
+          if (a.bias) {
+            g = g + a.bias[(int64_t)e * 2 * a.I + col];
+            u = u + a.bias[(int64_t)e * 2 * a.I + a.I + col];
+          }
           // y1 is rounded once to bf16; requantisation starts from that value
           y[m][i] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
         }
@@ -310,7 +315,9 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
 #pragma unroll
             for (int n = 0; n < 4; n++) {
               const int col = nb * WN + 64 * wave + 16 * n + r16;
-              Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(acc[m][n][i] * alpha);
+              float v = acc[m][n][i] * alpha;
+              if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
+              Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(v);
             }
           }
         } else {
@@ -319,7 +326,9 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
 #pragma unroll
           for (int n = 0; n < 4; n++) {
             const int col = nb * WN + 64 * wave + 16 * n + r16;
-            const float y2 = bf16_to_f32(f32_to_bf16(acc[m][n][i] * alpha));
+            float v = acc[m][n][i] * alpha;
+            if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
+            const float y2 = bf16_to_f32(f32_to_bf16(v));
             const float c = __fmul_rn(wf, y2);
             const float cn = __shfl_xor(c, 1);
             if (route >= 0 && (r16 & 1) == 0) {
@@ -415,6 +424,7 @@ hipError_t launch_gemm1_wide(const Gemm1Params& p, hipStream_t stream) {
   a.W_sf = p.w1_sf;
   a.alpha = p.w1_alpha;
   a.alpha_up = p.w1_alpha_up;
+  a.bias = p.fc1_bias;
   a.K = p.H;
   a.rows_per_expert = 2 * p.I;
   a.I = p.I;
@@ -433,6 +443,7 @@ hipError_t launch_gemm2_wide(const Gemm2Params& p, hipStream_t stream) {
   a.W = p.w2;
   a.W_sf = p.w2_sf;
   a.alpha = p.w2_alpha;
+  a.bias = p.fc2_bias;
   a.K = p.I;
   a.rows_per_expert = p.H;
   a.I = p.I;

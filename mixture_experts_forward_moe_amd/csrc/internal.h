@@ -32,6 +32,7 @@ struct Gemm1Params {
   GateAct act;
   const float* fc2_input_scale;
   const float* per_token_scale;  // W4A4 only; NULL: none
+  const float* fc1_bias;         // NULL, or fp32 [E_l, 2I]
   void* y1;
   uint8_t* y1_sf;
 };
@@ -43,6 +44,7 @@ struct Gemm2Params {
   const uint8_t* w2;
   const uint8_t* w2_sf;
   const float* w2_alpha;
+  const float* fc2_bias;  // NULL, or fp32 [E_l, H]
   int H, I;
   uint16_t* y2;
   const float* topk_weights;
@@ -79,6 +81,8 @@ struct DecodeParams {
   const uint8_t *w1, *w1_sf;
   const float* w1_alpha;
   const float* w1_alpha_up;  // NULL: w1_alpha for the up half too
+  const float* fc1_bias;     // NULL, or fp32 [E_l, 2I]
+  const float* fc2_bias;     // NULL, or fp32 [E_l, H]
   const uint8_t *w2, *w2_sf;
   const float* w2_alpha;
   int H, I;

@@ -39,6 +39,7 @@ struct StreamArgs {
   const uint8_t* W_sf;
   const float* alpha;
   const float* alpha_up;  // GEMM1: the up half's scale (NULL: alpha)
+  const float* bias;      // NULL, or fp32 [E, 2I] (GEMM1: gate then up) / [E, H] (GEMM2)
   int K;
   int rows_per_expert;
   int I;
@@ -166,7 +167,12 @@ __global__ __launch_bounds__(ST_THREADS) void gemm1_stream_kernel(const StreamAr
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int row = 4 * q + i;
-        const float y = gated_act_f32(ag[i] * al, au[i] * alu, a.act);
+        float gs = ag[i] * al, us = au[i] * alu;
+        if (a.bias) {
+          gs = gs + a.bias[(int64_t)e * 2 * a.I + col];
+          us = us + a.bias[(int64_t)e * 2 * a.I + a.I + col];
+        }
+        const float y = gated_act_f32(gs, us, a.act);
         if (row < valid) a.Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(y);
       }
     }
@@ -219,11 +225,15 @@ __global__ __launch_bounds__(ST_THREADS) void gemm2_stream_kernel(const StreamAr
           const int pt = tile_of(f);
           const int slot0 = pt * 16;
           const int valid = a.tile_limit[pt] - slot0;
-          const float al = a.alpha[a.tile_expert[pt]];
+          const int te = a.tile_expert[pt];
+          const float al = a.alpha[te];
+          const float bv = a.bias ? a.bias[(int64_t)te * a.n_out + 16 * g + c] : 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const int row = 4 * q + i;
-            const uint16_t v = f32_to_bf16(acc[i] * al);
+            float yv = acc[i] * al;
+            if (a.bias) yv = yv + bv;
+            const uint16_t v = f32_to_bf16(yv);
             if (row < valid) {
               if (a.out) y2s[(slot0 + row) * 16 + c] = v;
               else a.Y[(int64_t)(slot0 + row) * a.n_out + 16 * g + c] = v;
@@ -267,6 +277,7 @@ hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream) {
   a.W_sf = p.w1_sf;
   a.alpha = p.w1_alpha;
   a.alpha_up = p.w1_alpha_up;
+  a.bias = p.fc1_bias;
   a.K = p.H;
   a.rows_per_expert = 2 * p.I;
   a.I = p.I;
@@ -292,6 +303,7 @@ hipError_t launch_gemm2_stream(const Gemm2Params& p, int accumulate, hipStream_t
   a.W = p.w2;
   a.W_sf = p.w2_sf;
   a.alpha = p.w2_alpha;
+  a.bias = p.fc2_bias;
   a.K = p.I;
   a.rows_per_expert = p.H;
   a.I = p.I;

@@ -46,6 +46,8 @@ class DeviceProblem:
         self.fc2 = dev(np.array([p.fc2_input_scale], np.float32)) if p.mode == oracle.W4A4 else None
         self.w1_alpha_up = None if p.w1_alpha_up is None else dev(p.w1_alpha_up)
         self.pts = None if p.per_token_scale is None else dev(p.per_token_scale)
+        self.fc1_bias = None if p.fc1_bias is None else dev(p.fc1_bias)
+        self.fc2_bias = None if p.fc2_bias is None else dev(p.fc2_bias)
 
     def forward(self, out=None, tile=0, **kw):
         p = self.p
@@ -56,7 +58,8 @@ class DeviceProblem:
                         p.local_expert_offset, p.mode, out, p.H, p.I, tile=tile,
                         swiglu_alpha=p.swiglu_alpha, swiglu_beta=p.swiglu_beta, swiglu_limit=p.swiglu_limit,
                         activation=p.activation, situ_beta=p.situ_beta, situ_linear_beta=p.situ_linear_beta,
-                        w1_alpha_up=self.w1_alpha_up, per_token_scale=self.pts,
+                        w1_alpha_up=self.w1_alpha_up, per_token_scale=self.pts, fc1_bias=self.fc1_bias,
+                        fc2_bias=self.fc2_bias,
                         fc2_input_scale=self.fc2, routed_scaling_factor=p.routed_scaling_factor, **kw)
         return out
 

@@ -103,7 +103,7 @@ def test_activation_argument_checks():
     p = ctypes.byref(_plan())
     F = FAKE
     g = lambda act, a=1.0, b=0.0, lim=moe.FLT_MAX, sb=0.0, slb=0.0, pts=None: L.moe_grouped_gemm1_act(
-        0, F, None, 0, p, F, F, F, None, 256, 512, act, a, b, lim, sb, slb, None, pts, F, None, None)
+        0, F, None, 0, p, F, F, F, None, 256, 512, act, a, b, lim, sb, slb, None, pts, None, F, None, None)
     assert g(moe.ACT_RELU2) == UNSUPPORTED                         # non-gated GEMM1 is not built
     assert g(7) == INVALID                                         # unknown activation
     assert g(moe.ACT_GEGLU_TANH, a=1.702) == INVALID               # GeGLU takes no SwiGLU parameters

@@ -80,7 +80,8 @@ def test_gemm1_and_gemm2_stages(name, tile):
     y1_sf = None if s1sf is None else torch.zeros(s1sf, dtype=torch.uint8, device="cuda")
     moe.moe_grouped_gemm1_act(p.mode, d.x, d.x_sf, plan, d.w1, d.w1_sf, d.w1_alpha, p.H, p.I, y1, y1_sf,
                               p.activation, p.swiglu_alpha, p.swiglu_beta, p.swiglu_limit, p.situ_beta,
-                              p.situ_linear_beta, d.fc2, w1_alpha_up=d.w1_alpha_up, per_token_scale=d.pts)
+                              p.situ_linear_beta, d.fc2, w1_alpha_up=d.w1_alpha_up, per_token_scale=d.pts,
+                              fc1_bias=d.fc1_bias)
     torch.cuda.synchronize()
     valid = rplan.permuted_to_expanded >= 0
     gq = host(y1, dt1)[valid]
@@ -99,7 +100,8 @@ def test_gemm1_and_gemm2_stages(name, tile):
         assert agree >= 0.98
     # GEMM2 from the oracle's y1, so that it is checked on its own
     y2 = torch.zeros((slots, p.H), dtype=torch.int16, device="cuda")
-    moe.moe_grouped_gemm2(p.mode, dev(ry1), dev(ry1_sf), plan, d.w2, d.w2_sf, d.w2_alpha, p.H, p.I, y2=y2)
+    moe.moe_grouped_gemm2(p.mode, dev(ry1), dev(ry1_sf), plan, d.w2, d.w2_sf, d.w2_alpha, p.H, p.I, y2=y2,
+                          fc2_bias=d.fc2_bias)
     torch.cuda.synchronize()
     check_close(host(y2, np.uint16)[valid], ry2[valid], oracle.W4A16, f"{name} y2")
 
@@ -153,14 +155,17 @@ SCALED = ["w4a16_basic", "w4a16_wide", "w4a16_stream", "w4a4_offset", "w4a4_tall
 
 
 def scaled_problem(name):
-    """A copy of a case with its own up-half scales, per-token scales (W4A4)
-    and a routed_scaling_factor other than 1."""
+    """A copy of a case with its own up-half scales, per-token scales (W4A4),
+    FC1 / FC2 biases and a routed_scaling_factor other than 1."""
     import copy
     p = copy.copy(problem(name))
     rng = np.random.default_rng(70)
     p.w1_alpha_up = (p.w1_alpha * rng.uniform(0.5, 2.0, p.w1_alpha.shape)).astype(np.float32)
     if p.mode == oracle.W4A4:
         p.per_token_scale = rng.uniform(0.25, 4.0, p.M).astype(np.float32)
+    p.fc1_bias = rng.normal(0.0, 0.05, (p.num_local_experts, 2 * p.I)).astype(np.float32)
+    p.fc2_bias = rng.normal(0.0, 0.05, (p.num_local_experts, p.H)).astype(np.float32)
+    if p.mode == oracle.W4A4:
         oracle.set_fc2_input_scale(p, oracle.fc2_input_scale(p))   # calibrated on the scaled FC1 output
     p.routed_scaling_factor = 1.75
     return p
@@ -169,9 +174,9 @@ def scaled_problem(name):
 @pytest.mark.parametrize("name", SCALED)
 @pytest.mark.parametrize("tile", [0, 16, 128])
 def test_scales_and_routed_scaling(name, tile):
-    """The up half's own per-expert scale, the W4A4 per-token input row scale
-    and routed_scaling_factor != 1 through every GEMM1 kernel and both
-    finalize modes."""
+    """The up half's own per-expert scale, the W4A4 per-token input row scale,
+    FC1 / FC2 biases and routed_scaling_factor != 1 through every GEMM1 and
+    GEMM2 kernel and both finalize modes."""
     import torch
 
     import mixture_experts_forward_moe_amd as moe
@@ -228,6 +233,9 @@ def decode_case(case):
         wl = synth.small_workload(oracle.W4A16, 7, 2048, 1024, 32, 16, 4, 61, offset=4)
         p = oracle.quantize_problem(synth.make_raw(wl))
         p.w1_alpha_up = (p.w1_alpha * np.float32(1.5)).astype(np.float32)
+        rng = np.random.default_rng(61)
+        p.fc1_bias = rng.normal(0.0, 0.05, (p.num_local_experts, 2 * p.I)).astype(np.float32)
+        p.fc2_bias = rng.normal(0.0, 0.05, (p.num_local_experts, p.H)).astype(np.float32)
         p.routed_scaling_factor = 2.5
         return p
     elif case == "geglu":
