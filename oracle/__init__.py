@@ -19,7 +19,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 W4A16, W4A4, MXFP8_MXFP4 = 0, 1, 2
 ELEM_E4M3, ELEM_E2M1 = 0, 1
-ACT_SWIGLU, ACT_GEGLU_TANH = 0, 1   # FC1 activations (SiTU is SwiGLU with situ_beta > 0)
+ACT_SWIGLU, ACT_GEGLU_TANH, ACT_RELU2 = 0, 1, 2   # FC1 activations (SiTU: SwiGLU with situ_beta > 0;
+#                                                 ReLU^2 is non-gated, W1 has I rows)
 
 
 def build(force: bool = True) -> str:
@@ -388,8 +389,8 @@ def quantize_problem(raw, calibrate: bool = True) -> Problem:
         a1 = np.ones(E, np.float32)
         a2 = np.ones(E, np.float32)
     else:
-        w1 = np.zeros((E, 2 * I, H // 2), np.uint8)
-        w1_sf = np.zeros((E, 2 * I, H // 16), np.uint8)
+        w1 = np.zeros((E, raw.w1.shape[1], H // 2), np.uint8)
+        w1_sf = np.zeros((E, raw.w1.shape[1], H // 16), np.uint8)
         w2 = np.zeros((E, H, I // 2), np.uint8)
         w2_sf = np.zeros((E, H, I // 16), np.uint8)
         a1 = np.zeros(E, np.float32)

@@ -50,7 +50,7 @@
 
 enum { ORC_W4A16 = 0, ORC_W4A4 = 1, ORC_MXFP8_MXFP4 = 2 };
 enum { ORC_ELEM_E4M3 = 0, ORC_ELEM_E2M1 = 1 };
-enum { ORC_ACT_SWIGLU = 0, ORC_ACT_GEGLU_TANH = 1 };
+enum { ORC_ACT_SWIGLU = 0, ORC_ACT_GEGLU_TANH = 1, ORC_ACT_RELU2 = 2 };
 
 /* ------------------------------------------------------------------------ */
 /* Number formats (OCP MX v1.0 / OCP FP8, as named by the pages)            */
@@ -370,12 +370,13 @@ typedef struct {
   float swiglu_alpha, swiglu_beta, swiglu_limit;
   float fc2_input_scale; /* W4A4: global scale of the FC1-output requantisation */
   float routed_scaling_factor;
-  int activation;         /* ORC_ACT_SWIGLU (SwiGLU, or SiTU when situ_beta > 0) | ORC_ACT_GEGLU_TANH */
+  int activation;         /* ORC_ACT_SWIGLU (SwiGLU, or SiTU when situ_beta > 0) | ORC_ACT_GEGLU_TANH |
+                             ORC_ACT_RELU2 (non-gated: W1 has I rows) */
   float situ_beta;        /* > 0 selects SiTU; 0 = unset */
   float situ_linear_beta; /* > 0: SiTU tanh clamp of the up branch; 0 = unset */
   const float* w1_alpha_up;     /* NULL, or fp32 [E_l]: the up half's own scale */
   const float* per_token_scale; /* NULL, or fp32 [M] (W4A4): GEMM1 input row scale */
-  const float* fc1_bias;        /* NULL, or fp32 [E_l, 2I]: GEMM1 bias, gate then up */
+  const float* fc1_bias;        /* NULL, or fp32 [E_l, 2I]: GEMM1 bias, gate then up ([E_l, I] for ReLU^2) */
   const float* fc2_bias;        /* NULL, or fp32 [E_l, H]: GEMM2 bias */
 } orc_moe_t;
 
@@ -417,8 +418,11 @@ static void dequant_w_row(int mode, const uint8_t* q, const uint8_t* sf, int K, 
   }
 }
 
+/* W1 rows per expert: gate and up (2I), or I for the non-gated ReLU^2. */
+static int w1_rows(const orc_moe_t* p) { return p->activation == ORC_ACT_RELU2 ? p->I : 2 * p->I; }
+
 static const uint8_t* w1_row(const orc_moe_t* p, int le, int n, const uint8_t** sf) {
-  int64_t row = (int64_t)le * 2 * p->I + n;
+  int64_t row = (int64_t)le * w1_rows(p) + n;
   *sf = p->w1_sf + row * (p->H / sf_block(p->mode));
   return p->w1 + row * (p->H / 2);
 }
@@ -508,6 +512,25 @@ static void gate_up(const orc_moe_t* p, int le, int64_t t, int j, double G, doub
   *u = uv;
 }
 
+/* FC1 output j of token t through local expert le, before its bf16
+ * rounding, from the fp64 sums of its W1 rows: the gated activation of the
+ * gate / up pair (G from row j, U from row I + j), or for ReLU^2
+ * ("flashinfer.fused_moe.cute_dsl_fused_moe", Parameters activation_type:
+ * non-gated Relu2) max(h, 0)^2 of the single row j, h scaled like the gate
+ * (expert scale, per-token scale, bias) in fp32. */
+static double fc1_out(const orc_moe_t* p, int le, int64_t t, int j, double G, double U) {
+  if (p->activation == ORC_ACT_RELU2) {
+    float h = scale_acc(G, p->w1_alpha[le]);
+    if (p->per_token_scale) h = h * p->per_token_scale[t];
+    if (p->fc1_bias) h = h + p->fc1_bias[(int64_t)le * p->I + j];
+    double r = h > 0.0f ? (double)h : 0.0;
+    return r * r;
+  }
+  float g, u;
+  gate_up(p, le, t, j, G, U, &g, &u);
+  return gated_act(p, g, u);
+}
+
 /* GEMM2 output of column c through local expert le before its bf16
  * rounding: the fp32 accumulator times w2_alpha, plus the expert's fc2 bias
  * when given ("flashinfer.fused_moe.cutlass_fused_moe", Parameters
@@ -527,9 +550,7 @@ static void swiglu_row_and_requant(const orc_moe_t* p, int le, int64_t t, const 
   int I = p->I;
   float* y = (float*)malloc((size_t)I * sizeof(float));
   for (int j = 0; j < I; j++) {
-    float g, u;
-    gate_up(p, le, t, j, G[j], U[j], &g, &u);
-    uint16_t b = orc_bf16_round(gated_act(p, g, u));
+    uint16_t b = orc_bf16_round(fc1_out(p, le, t, j, G[j], U[j]));
     if (y1_bf16) y1_bf16[j] = b;
     y[j] = orc_bf16_value(b);
   }
@@ -564,13 +585,13 @@ void orc_gemm1_route(const orc_moe_t* p, int64_t t, int le, uint16_t* y1_bf16, u
   int H = p->H, I = p->I;
   double* a = (double*)malloc((size_t)H * sizeof(double));
   double* G = (double*)malloc((size_t)I * sizeof(double));
-  double* U = (double*)malloc((size_t)I * sizeof(double));
+  double* U = (double*)calloc((size_t)I, sizeof(double));
   dequant_x_row(p, t, a);
 #pragma omp parallel
   {
     double* w = (double*)malloc((size_t)H * sizeof(double));
 #pragma omp for schedule(static)
-    for (int n = 0; n < 2 * I; n++) {
+    for (int n = 0; n < w1_rows(p); n++) {
       const uint8_t* sf;
       const uint8_t* q = w1_row(p, le, n, &sf);
       dequant_w_row(p->mode, q, sf, H, w);
@@ -660,12 +681,12 @@ void orc_forward_tokens(const orc_moe_t* p, const int32_t* tokens, int ntok, int
   free(acc);
 }
 
-/* Decoded weights of one expert: W1 [2I, H] and W2 [H, I] in fp64. */
+/* Decoded weights of one expert: W1 [2I (or I), H] and W2 [H, I] in fp64. */
 static void dequant_expert(const orc_moe_t* p, int le, double* wd1, double* wd2) {
   int H = p->H, I = p->I;
   if (wd1) {
 #pragma omp parallel for schedule(static)
-    for (int n = 0; n < 2 * I; n++) {
+    for (int n = 0; n < w1_rows(p); n++) {
       const uint8_t* sf;
       const uint8_t* q = w1_row(p, le, n, &sf);
       dequant_w_row(p->mode, q, sf, H, wd1 + (int64_t)n * H);
@@ -713,7 +734,7 @@ void orc_forward_plan(const orc_moe_t* p, int tile, int32_t* e2p, int32_t* p2e,
         int64_t t = p2e[slot] / p->top_k;
         dequant_x_row(p, t, a);
         for (int n = 0; n < I; n++) G[n] = dot(a, wd1 + (int64_t)n * H, H);
-        for (int n = 0; n < I; n++) U[n] = dot(a, wd1 + (int64_t)(I + n) * H, H);
+        for (int n = 0; n < I; n++) U[n] = w1_rows(p) > I ? dot(a, wd1 + (int64_t)(I + n) * H, H) : 0.0;
         uint16_t* yb = NULL;
         uint8_t *yq = NULL, *ys = NULL;
         if (p->mode == ORC_W4A16) {
@@ -763,9 +784,8 @@ float orc_fc2_input_scale(const orc_moe_t* p) {
         if (p->topk_ids[r] - p->local_expert_offset != le) continue;
         dequant_x_row(p, r / k, a);
         for (int n = 0; n < I; n++) {
-          float g, u;
-          gate_up(p, le, r / k, n, dot(a, wd1 + (int64_t)n * H, H), dot(a, wd1 + (int64_t)(I + n) * H, H), &g, &u);
-          uint16_t b = orc_bf16_round(gated_act(p, g, u));
+          const double U = w1_rows(p) > I ? dot(a, wd1 + (int64_t)(I + n) * H, H) : 0.0;
+          uint16_t b = orc_bf16_round(fc1_out(p, le, r / k, n, dot(a, wd1 + (int64_t)n * H, H), U));
           float v = fabsf(orc_bf16_value(b));
           if (v > local) local = v;
         }

@@ -124,7 +124,7 @@ class Workload:
     swiglu_alpha: float = 1.0
     swiglu_beta: float = 0.0
     swiglu_limit: float = float(np.finfo(np.float32).max)
-    activation: int = 0               # 0 SwiGLU (SiTU when situ_beta > 0), 1 GeGLU-tanh
+    activation: int = 0               # 0 SwiGLU (SiTU when situ_beta > 0), 1 GeGLU-tanh, 2 ReLU^2
     situ_beta: float = 0.0
     situ_linear_beta: float = 0.0
     x_std: float = 1.0
@@ -179,7 +179,8 @@ def make_raw(wl: Workload, weights: bool = True) -> RawInputs:
     raw = RawInputs(wl, x, ids, w)
     if weights:
         E = wl.num_local_experts
-        raw.w1 = normal_bf16(wl.seed, STREAM_W1, (E, 2 * wl.I, wl.H), 0.0, wl.w_std)
+        rows = wl.I if wl.activation == 2 else 2 * wl.I   # ReLU^2 is non-gated: I rows
+        raw.w1 = normal_bf16(wl.seed, STREAM_W1, (E, rows, wl.H), 0.0, wl.w_std)
         raw.w2 = normal_bf16(wl.seed, STREAM_W2, (E, wl.H, wl.I), 0.0, wl.w_std)
     return raw
 

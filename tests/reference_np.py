@@ -154,6 +154,18 @@ def forward_tokens(p, tokens):
             W1d, W2d = w1d_cache[le]
             gu = W1d @ a
             al1 = np.float32(p.w1_alpha[le])
+            if getattr(p, "activation", 0) == 2:
+                # non-gated ReLU^2 (torch's relu) of the single row, scaled like the gate
+                h = (gu.astype(np.float32) * al1).astype(np.float32)
+                if getattr(p, "per_token_scale", None) is not None:
+                    h = (h * np.float32(p.per_token_scale[t])).astype(np.float32)
+                if getattr(p, "fc1_bias", None) is not None:
+                    h = (h + p.fc1_bias[le]).astype(np.float32)
+                r = torch.relu(torch.from_numpy(h.astype(np.float64)))
+                y1 = bf16_vals(to_bf16_bits((r * r).numpy()))
+            else:
+                y1 = None
+            al1 = np.float32(p.w1_alpha[le])
             alu = al1 if getattr(p, "w1_alpha_up", None) is None else np.float32(p.w1_alpha_up[le])
             g = (gu[:I].astype(np.float32) * al1).astype(np.float32)
             u = (gu[I:].astype(np.float32) * alu).astype(np.float32)
@@ -164,7 +176,8 @@ def forward_tokens(p, tokens):
             if getattr(p, "fc1_bias", None) is not None:
                 g = (g + p.fc1_bias[le, :I]).astype(np.float32)
                 u = (u + p.fc1_bias[le, I:]).astype(np.float32)
-            y1 = bf16_vals(to_bf16_bits(gated_act(p, g, u)))
+            if y1 is None:
+                y1 = bf16_vals(to_bf16_bits(gated_act(p, g, u)))
             if p.mode == W4A16:
                 a2 = y1
             elif p.mode == W4A4:

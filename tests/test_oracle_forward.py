@@ -42,6 +42,10 @@ SMALL = [
                         situ_linear_beta=0.08)),
     (oracle.W4A4, dict(M=9, H=64, I=64, E=8, El=8, k=2, seed=29, situ_beta=0.1)),
     (oracle.MXFP8_MXFP4, dict(M=9, H=96, I=64, E=8, El=8, k=2, seed=30, activation=oracle.ACT_GEGLU_TANH)),
+    # the non-gated ReLU^2 (W1 has I rows)
+    (oracle.W4A16, dict(M=10, H=64, I=64, E=8, El=6, k=3, seed=31, offset=2, activation=oracle.ACT_RELU2)),
+    (oracle.W4A4, dict(M=9, H=64, I=64, E=8, El=8, k=2, seed=36, activation=oracle.ACT_RELU2)),
+    (oracle.MXFP8_MXFP4, dict(M=9, H=96, I=64, E=8, El=8, k=2, seed=37, activation=oracle.ACT_RELU2)),
 ]
 
 
@@ -232,6 +236,27 @@ def test_fc_biases_closed_forms():
         want1 = ref.to_bf16_bits(np.array([oracle.swiglu(float(g), float(u)) for g, u in zip(bg, bu)]))
         assert np.array_equal(y1[slot], want1)
         assert np.array_equal(y2[slot], ref.to_bf16_bits(p.fc2_bias[le].astype(np.float64)))
+
+
+def test_relu2_closed_forms():
+    p = _problem(oracle.W4A16, M=6, H=64, I=32, E=4, El=4, k=2, seed=65, activation=oracle.ACT_RELU2)
+    assert p.w1.shape[1] == p.I                 # non-gated: I rows of W1
+    plan, y1, _, _, _ = oracle.forward_plan(p, 4)
+    valid = plan.permuted_to_expanded >= 0
+    v = synth.bf16_to_f32(y1[valid])
+    assert np.all(v >= 0) and np.any(v == 0) and np.any(v > 0)
+    # degree-2 homogeneity: doubling the expert scale quadruples y1 exactly
+    p.w1_alpha = (p.w1_alpha * np.float32(2.0)).astype(np.float32)
+    _, y1b, _, _, _ = oracle.forward_plan(p, 4)
+    assert np.array_equal(v * 4, synth.bf16_to_f32(y1b[valid]))
+    # all-zero weight codes with a bias: y1 = bf16(relu(b)^2) exactly
+    p.w1 = np.zeros_like(p.w1)
+    p.fc1_bias = np.random.default_rng(66).normal(0, 0.5, (p.num_local_experts, p.I)).astype(np.float32)
+    plan, y1c, _, _, _ = oracle.forward_plan(p, 4)
+    for slot in np.nonzero(plan.permuted_to_expanded >= 0)[0]:
+        le = int(p.topk_ids.reshape(-1)[plan.permuted_to_expanded[slot]]) - p.local_expert_offset
+        b = np.maximum(p.fc1_bias[le].astype(np.float64), 0.0)
+        assert np.array_equal(y1c[slot], ref.to_bf16_bits(b * b))
 
 
 def test_power_of_two_w2_alpha_scales_y2_exactly():
