@@ -51,6 +51,7 @@ class GpuInputs:
         import synth
         self.wl = wl
         E, H, I, M = wl.num_local_experts, wl.H, wl.I, wl.M
+        R1 = I if wl.activation == 2 else 2 * I   # W1 rows: ReLU^2 is non-gated
         raw = synth.make_raw(wl)
         self.topk_ids_np = raw.topk_ids
         dev = "cuda"
@@ -62,11 +63,11 @@ class GpuInputs:
         self.x_sf = None
         self.fc2 = None
         if wl.mode == moe.MXFP8_MXFP4:
-            self.w1 = torch.empty((E, 2 * I, H // 2), **u8)
-            self.w1_sf = torch.empty((E, 2 * I, H // 32), **u8)
+            self.w1 = torch.empty((E, R1, H // 2), **u8)
+            self.w1_sf = torch.empty((E, R1, H // 32), **u8)
             self.w2 = torch.empty((E, H, I // 2), **u8)
             self.w2_sf = torch.empty((E, H, I // 32), **u8)
-            moe.moe_quantize_mx(w1b, E * 2 * I, H, 1, self.w1, self.w1_sf)
+            moe.moe_quantize_mx(w1b, E * R1, H, 1, self.w1, self.w1_sf)
             moe.moe_quantize_mx(w2b, E * H, I, 1, self.w2, self.w2_sf)
             self.w1_alpha = torch.ones(E, dtype=torch.float32, device=dev)
             self.w2_alpha = torch.ones(E, dtype=torch.float32, device=dev)
@@ -74,14 +75,14 @@ class GpuInputs:
             self.x_sf = torch.empty((M, H // 32), **u8)
             moe.moe_quantize_mx(xb, M, H, 0, self.x, self.x_sf)
         else:
-            self.w1 = torch.empty((E, 2 * I, H // 2), **u8)
-            self.w1_sf = torch.empty((E, 2 * I, H // 16), **u8)
+            self.w1 = torch.empty((E, R1, H // 2), **u8)
+            self.w1_sf = torch.empty((E, R1, H // 16), **u8)
             self.w2 = torch.empty((E, H, I // 2), **u8)
             self.w2_sf = torch.empty((E, H, I // 16), **u8)
             self.w1_alpha = torch.empty(E, dtype=torch.float32, device=dev)
             self.w2_alpha = torch.empty(E, dtype=torch.float32, device=dev)
             moe.moe_nvfp4_global_scale(w1b, E, self.w1_alpha)
-            moe.moe_quantize_nvfp4(w1b, E, 2 * I, H, self.w1_alpha, self.w1, self.w1_sf)
+            moe.moe_quantize_nvfp4(w1b, E, R1, H, self.w1_alpha, self.w1, self.w1_sf)
             moe.moe_nvfp4_global_scale(w2b, E, self.w2_alpha)
             moe.moe_quantize_nvfp4(w2b, E, H, I, self.w2_alpha, self.w2, self.w2_sf)
             if wl.mode == moe.W4A4:
@@ -238,7 +239,8 @@ def w4a16_bytes(wl, routes, active):
     read, y2 written and read; routing ids and weights read; the output
     written once."""
     H, I = wl.H, wl.I
-    w1 = 2 * I * H // 2 + 2 * I * H // 16
+    R1 = I if wl.activation == 2 else 2 * I   # W1 rows: ReLU^2 is non-gated
+    w1 = R1 * H // 2 + R1 * H // 16
     w2 = H * I // 2 + H * I // 16
     act = routes * (2 * H + 2 * 2 * I + 2 * 2 * H)
     io = wl.M * wl.top_k * 8 + wl.M * H * 2
@@ -439,16 +441,17 @@ def main():
         import dataclasses
         acts = {}
         for name, kw in (("geglu_tanh", dict(activation=1)), ("situ", dict(situ_beta=0.5, situ_linear_beta=1.0)),
-                         ("swiglu_scaled", dict())):
+                         ("relu2", dict(activation=2)), ("swiglu_scaled", dict())):
             scaled = name == "swiglu_scaled"
             wd = dataclasses.replace(wl, **kw)
             log(f"bench: {wd.name} with {name}: {max(20, args.steps // 4)} steps (graph replay)")
             rd = time_graph(wd, max(20, args.steps // 4), max(4, args.warmup // 4), args.copies, scaled=scaled)
-            fd = by["forward"] / (rd["gpu_ms_per_step"] * 1e-3) / 1e9
+            fd = w4a16_bytes(wd, routes, active)["forward"] / (rd["gpu_ms_per_step"] * 1e-3) / 1e9
             wp = dataclasses.replace(synth.WORKLOADS["w4a16_prefill"], swiglu_limit=float(np.finfo(np.float32).max),
                                      **kw)
             rp = time_phases(wp, 10, 3, args.copies, scaled=scaled)
-            g1 = 4.0 * wp.H * wp.I * rp["local_routes"] / (rp["phase_ms"]["gemm1"] * 1e-3) / 1e12
+            g1 = (2.0 if wp.activation == 2 else 4.0) * wp.H * wp.I * rp["local_routes"] / (
+                rp["phase_ms"]["gemm1"] * 1e-3) / 1e12
             if scaled:
                 kw = {"w1_alpha_up": "1.5 x w1_alpha", "fc1_bias": 0.01, "fc2_bias": 0.01,
                       "routed_scaling_factor": 1.75}

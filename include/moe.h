@@ -171,7 +171,7 @@ moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, cons
 typedef enum moe_activation {
   MOE_ACT_SWIGLU = 0,      /* gated SwiGLU with swiglu_alpha / beta / limit; SiTU when situ_beta > 0 */
   MOE_ACT_GEGLU_TANH = 1,  /* gated GeGLU, tanh-approximate GELU of the gate */
-  MOE_ACT_RELU2 = 2        /* non-gated ReLU^2: not implemented, MOE_ERR_UNSUPPORTED */
+  MOE_ACT_RELU2 = 2        /* non-gated ReLU^2: W1 holds I rows, y1[j] = max(h_j, 0)^2 */
 } moe_activation_t;
 
 /* moe_grouped_gemm1_act: moe_grouped_gemm1_swiglu with the FC1 activation
@@ -194,12 +194,16 @@ typedef enum moe_activation {
  *       y1 = situ_beta * tanh(g / situ_beta) * sigmoid(g) * u',
  *       u' = situ_linear_beta * tanh(u / situ_linear_beta) if situ_linear_beta > 0, else u.
  *   MOE_ACT_GEGLU_TANH: y1 = g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3))) * u.
+ *   MOE_ACT_RELU2 (non-gated): w1 is [E_l, I, H/2] codes + [E_l, I, H/16 or
+ *       H/32] scales, one row per y1 column; y1[j] = max(h_j, 0)^2 with h_j
+ *       row j's accumulator scaled like a gate value (w1_alpha, per-token
+ *       scale, fc1_bias [E_l, I]).  w1_alpha_up must be NULL.
  * Everything else (inputs, layouts, requantisation, rounding once to bf16)
  * is as in moe_grouped_gemm1_swiglu.  MOE_ERR_INVALID_ARGUMENT: an unknown
  * activation; situ_beta or situ_linear_beta negative or not finite;
  * situ_linear_beta > 0 without situ_beta > 0; GeGLU or SiTU together with
- * non-default SwiGLU parameters (1, 0, FLT_MAX) or GeGLU with SiTU
- * parameters.  MOE_ERR_UNSUPPORTED: MOE_ACT_RELU2. */
+ * non-default SwiGLU parameters (1, 0, FLT_MAX), GeGLU or ReLU^2 with SiTU
+ * parameters, ReLU^2 with w1_alpha_up. */
 moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const uint8_t* x_sf,
                                    int64_t x_row_stride, const moe_plan_t* plan, const uint8_t* w1,
                                    const uint8_t* w1_sf, const float* w1_alpha, const float* w1_alpha_up, int H,

@@ -72,17 +72,17 @@ moe_status_t shape_check(int H, int I, int mode) {
 // moe.h, moe_grouped_gemm1_act).
 moe_status_t make_act(int activation, float alpha, float beta, float limit, float situ_beta, float situ_lin,
                       GateAct* out) {
-  if (activation == MOE_ACT_RELU2) return MOE_ERR_UNSUPPORTED;
-  if (activation != MOE_ACT_SWIGLU && activation != MOE_ACT_GEGLU_TANH) return MOE_ERR_INVALID_ARGUMENT;
+  if (activation != MOE_ACT_SWIGLU && activation != MOE_ACT_GEGLU_TANH && activation != MOE_ACT_RELU2)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (!(limit > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
   if (!(situ_beta >= 0.0f) || !std::isfinite(situ_beta)) return MOE_ERR_INVALID_ARGUMENT;
   if (!(situ_lin >= 0.0f) || !std::isfinite(situ_lin)) return MOE_ERR_INVALID_ARGUMENT;
   if (situ_lin > 0.0f && !(situ_beta > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
   const bool swiglu_default = alpha == 1.0f && beta == 0.0f && limit == FLT_MAX;
   GateAct a = {ACT_SWIGLU, alpha, beta, limit, situ_beta, situ_lin};
-  if (activation == MOE_ACT_GEGLU_TANH) {
+  if (activation == MOE_ACT_GEGLU_TANH || activation == MOE_ACT_RELU2) {
     if (!swiglu_default || situ_beta > 0.0f) return MOE_ERR_INVALID_ARGUMENT;
-    a.kind = ACT_GEGLU_TANH;
+    a.kind = activation == MOE_ACT_RELU2 ? ACT_RELU2 : ACT_GEGLU_TANH;
   } else if (situ_beta > 0.0f) {
     if (!swiglu_default) return MOE_ERR_INVALID_ARGUMENT;
     a.kind = ACT_SITU;
@@ -195,6 +195,7 @@ moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const u
   Gemm1Params p = {};
   s = make_act(activation, swiglu_alpha, swiglu_beta, swiglu_limit, situ_beta, situ_linear_beta, &p.act);
   if (s != MOE_OK) return s;
+  if (p.act.kind == ACT_RELU2 && w1_alpha_up) return MOE_ERR_INVALID_ARGUMENT;  // no up half
   p.mode = mode;
   p.x = x;
   p.x_sf = x_sf;
@@ -349,6 +350,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   s = make_act(opts->activation, opts->swiglu_alpha, opts->swiglu_beta, opts->swiglu_limit, opts->situ_beta,
                opts->situ_linear_beta, &act);
   if (s != MOE_OK) return s;
+  if (act.kind == ACT_RELU2 && opts->w1_alpha_up) return MOE_ERR_INVALID_ARGUMENT;  // no up half
   const int tile = opts->tile ? opts->tile : moe_default_tile(M, top_k, num_local_experts, quant_mode);
   if (!pow2_in(tile, 16, 256)) return MOE_ERR_UNSUPPORTED;
   const size_t need = moe_workspace_size(M, H, I, top_k, num_local_experts, tile, quant_mode, opts->finalize_mode);

@@ -69,6 +69,7 @@ struct DecArgs {
   const uint8_t* w2_sf;
   const float* w2_alpha;
   int H, I;
+  int ip;                // W1 row pairs per expert: I (gated), I/2 (ReLU^2: rows j, I/2 + j)
   GateAct act;          // FC1 activation
   uint16_t* y1;          // [slots, I]
   uint16_t* y2;          // [slots, H]
@@ -392,8 +393,8 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
     const int e = tile_owner(P, a.El, pt);
     const int slot0 = pt * DEC_T;
     const int valid = min(DEC_T, P.tbase[e] * DEC_T + P.cnt[e] - slot0);
-    const int64_t rg = (int64_t)e * 2 * a.I + col;
-    const int64_t ru = rg + a.I;
+    const int64_t rg = (int64_t)e * 2 * a.ip + col;
+    const int64_t ru = rg + a.ip;
     const float al = a.w1_alpha[e];
     const float alu = a.w1_alpha_up ? a.w1_alpha_up[e] : al;
     for (int r0 = 0; r0 < valid; r0++) {
@@ -429,11 +430,16 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
         if (ch == 0) {
           float gs = g * al, us = u * alu;
           if (a.fc1_bias) {
-            gs = gs + a.fc1_bias[(int64_t)e * 2 * a.I + col + 16 * p];
-            us = us + a.fc1_bias[(int64_t)e * 2 * a.I + a.I + col + 16 * p];
+            gs = gs + a.fc1_bias[(int64_t)e * 2 * a.ip + col + 16 * p];
+            us = us + a.fc1_bias[(int64_t)e * 2 * a.ip + a.ip + col + 16 * p];
           }
-          const float y = gated_act_f32(gs, us, a.act);
-          a.y1[(int64_t)(slot0 + r0) * a.I + col + 16 * p] = f32_to_bf16(y);
+          uint16_t* yrow = a.y1 + (int64_t)(slot0 + r0) * a.I;
+          if (a.act.kind == ACT_RELU2) {  // non-gated: both rows are outputs
+            yrow[col + 16 * p] = f32_to_bf16(relu2_f32(gs));
+            yrow[a.ip + col + 16 * p] = f32_to_bf16(relu2_f32(us));
+          } else {
+            yrow[col + 16 * p] = f32_to_bf16(gated_act_f32(gs, us, a.act));
+          }
         }
       }
       __syncthreads();
@@ -710,6 +716,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   a.w2_alpha = p.w2_alpha;
   a.H = p.H;
   a.I = p.I;
+  a.ip = p.act.kind == ACT_RELU2 ? p.I / 2 : p.I;
   a.act = p.act;
   a.y1 = p.y1;
   a.y2 = p.y2;
@@ -732,7 +739,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const size_t lds1 = plan_lds(a.El, R) + sizeof(uint16_t) * DEC_ROWS * a.H + 16;
   // prefetch depth: the deepest that divides the K-step count
   const int ns1 = a.H / 512;
-  const dim3 g1(a.I / (16 * G1_NP), P), g2(a.H / 64, P);
+  const dim3 g1(a.ip / (16 * G1_NP), P), g2(a.H / 64, P);
   if (p.mark) p.mark(p.mark_ctx, 1);
   if (ns1 % G1_D == 0) dec_gemm1_kernel<G1_D, G1_NP><<<g1, DEC_THREADS, lds1, stream>>>(a);
   else if (ns1 % 2 == 0) dec_gemm1_kernel<2, G1_NP><<<g1, DEC_THREADS, lds1, stream>>>(a);

@@ -134,9 +134,9 @@ DEV float swiglu_f32(float g, float u, float alpha, float beta, float limit) {
 // The gated FC1 activation ("flashinfer.fused_moe.cute_dsl_fused_moe",
 // Parameters activation_type, swiglu_*, situ_beta, situ_linear_beta), one
 // block of kernel arguments shared by every GEMM1 epilogue.
-enum { ACT_SWIGLU = 0, ACT_GEGLU_TANH = 1, ACT_SITU = 2 };
+enum { ACT_SWIGLU = 0, ACT_GEGLU_TANH = 1, ACT_SITU = 2, ACT_RELU2 = 3 };
 struct GateAct {
-  int kind;                  // ACT_*
+  int kind;                  // ACT_* (ACT_RELU2: non-gated, each W1 row is an output)
   float alpha, beta, limit;  // SwiGLU
   float situ_beta;           // SiTU gate: situ_beta * tanh(g / situ_beta) * sigmoid(g)
   float situ_lin;            // SiTU up-branch clamp situ_lin * tanh(u / situ_lin); 0 = none
@@ -157,4 +157,10 @@ DEV float gated_act_f32(float g, float u, const GateAct& p) {
     return gate * up;
   }
   return swiglu_f32(g, u, p.alpha, p.beta, p.limit);
+}
+
+// ReLU^2 of one FC1 row (activation_type Relu2, non-gated): max(h, 0)^2.
+DEV float relu2_f32(float h) {
+  const float r = fmaxf(h, 0.0f);
+  return r * r;
 }

@@ -326,7 +326,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
   if constexpr (GEMM == 1) {
     const float alpha_u = a.alpha_up ? a.alpha_up[e] : alpha;
     const int col = j0 + wave * 16 + r16;  // output column of y1
-    float y[MT][4];
+    // gated: one output per gate / up pair; ReLU^2 (non-gated): the two
+    // rows of a pair are outputs col and a.I + col
+    const bool two = a.act.kind == ACT_RELU2;
+    float y[2][MT][4];
 #pragma unroll
     for (int m = 0; m < MT; m++)
 #pragma unroll
@@ -344,63 +347,74 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
           u = u + a.bias[(int64_t)e * 2 * a.I + a.I + col];
         }
         // y1 is rounded once to bf16; requantisation starts from that value
-        y[m][i] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
+        if (two) {
+          y[0][m][i] = bf16_to_f32(f32_to_bf16(relu2_f32(g)));
+          y[1][m][i] = bf16_to_f32(f32_to_bf16(relu2_f32(u)));
+        } else {
+          y[0][m][i] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
+          y[1][m][i] = 0.0f;
+        }
       }
-    if constexpr (MODE == M_W4A16) {
-      uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
+    auto store = [&](const float (&ys)[MT][4], const int cx) {
+      if constexpr (MODE == M_W4A16) {
+        uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
 #pragma unroll
-      for (int m = 0; m < MT; m++)
+        for (int m = 0; m < MT; m++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          int row = m * 16 + 4 * q + i;
-          if (row < valid) Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(y[m][i]);
-        }
-    } else if constexpr (MODE == M_W4A4) {
-      // NVFP4 with the global scale fc2_input_scale; a block is the 16
-      // columns of this wave's tile (the 16 lanes of one lane group)
-      const float gs = *a.fc2_scale;
-      uint8_t* Yq = reinterpret_cast<uint8_t*>(a.Y);
-#pragma unroll
-      for (int m = 0; m < MT; m++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          int row = m * 16 + 4 * q + i;
-          float bamax = warp_max16(fabsf(y[m][i]));
-          uint32_t sc = nvfp4_scale_code(bamax, gs);
-          uint32_t code = nvfp4_elem_code(y[m][i], e4m3_to_f32(sc), gs);
-          uint32_t other = __shfl_xor(code, 1);
-          if (row < valid) {
-            int64_t slot = slot0 + row;
-            if ((r16 & 1) == 0) Yq[slot * (a.n_out / 2) + col / 2] = (uint8_t)(code | (other << 4));
-            if (r16 == 0) a.Y_sf[slot * (a.n_out / 16) + col / 16] = (uint8_t)sc;
+          for (int i = 0; i < 4; i++) {
+            int row = m * 16 + 4 * q + i;
+            if (row < valid) Y[(int64_t)(slot0 + row) * a.n_out + cx] = f32_to_bf16(ys[m][i]);
           }
-        }
-    } else {
-      // MXFP8: a block of 32 columns spans this wave and its neighbour
+      } else if constexpr (MODE == M_W4A4) {
+        // NVFP4 with the global scale fc2_input_scale; a block is the 16
+        // columns of this wave's tile (the 16 lanes of one lane group)
+        const float gs = *a.fc2_scale;
+        uint8_t* Yq = reinterpret_cast<uint8_t*>(a.Y);
 #pragma unroll
-      for (int m = 0; m < MT; m++)
+        for (int m = 0; m < MT; m++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          float am = warp_max16(fabsf(y[m][i]));
-          if (r16 == 0) red[wave][m * 16 + 4 * q + i] = am;
-        }
-      __syncthreads();
-      uint8_t* Yq = reinterpret_cast<uint8_t*>(a.Y);
-#pragma unroll
-      for (int m = 0; m < MT; m++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          int row = m * 16 + 4 * q + i;
-          float am = fmaxf(red[wave][row], red[wave ^ 1][row]);
-          uint32_t code = mx_scale_code(am, 8);
-          uint32_t b = f32x2_to_e4m3x2_mx(y[m][i], 0.0f, code) & 255u;
-          if (row < valid) {
-            int64_t slot = slot0 + row;
-            Yq[slot * a.n_out + col] = (uint8_t)b;
-            if (r16 == 0 && (wave & 1) == 0) a.Y_sf[slot * (a.n_out / 32) + col / 32] = (uint8_t)code;
+          for (int i = 0; i < 4; i++) {
+            int row = m * 16 + 4 * q + i;
+            float bamax = warp_max16(fabsf(ys[m][i]));
+            uint32_t sc = nvfp4_scale_code(bamax, gs);
+            uint32_t code = nvfp4_elem_code(ys[m][i], e4m3_to_f32(sc), gs);
+            uint32_t other = __shfl_xor(code, 1);
+            if (row < valid) {
+              int64_t slot = slot0 + row;
+              if ((r16 & 1) == 0) Yq[slot * (a.n_out / 2) + cx / 2] = (uint8_t)(code | (other << 4));
+              if (r16 == 0) a.Y_sf[slot * (a.n_out / 16) + cx / 16] = (uint8_t)sc;
+            }
           }
-        }
-    }
+      } else {
+        // MXFP8: a block of 32 columns spans this wave and its neighbour
+        __syncthreads();  // the previous set's exchange has been read
+#pragma unroll
+        for (int m = 0; m < MT; m++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            float am = warp_max16(fabsf(ys[m][i]));
+            if (r16 == 0) red[wave][m * 16 + 4 * q + i] = am;
+          }
+        __syncthreads();
+        uint8_t* Yq = reinterpret_cast<uint8_t*>(a.Y);
+#pragma unroll
+        for (int m = 0; m < MT; m++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            int row = m * 16 + 4 * q + i;
+            float am = fmaxf(red[wave][row], red[wave ^ 1][row]);
+            uint32_t code = mx_scale_code(am, 8);
+            uint32_t b = f32x2_to_e4m3x2_mx(ys[m][i], 0.0f, code) & 255u;
+            if (row < valid) {
+              int64_t slot = slot0 + row;
+              Yq[slot * a.n_out + cx] = (uint8_t)b;
+              if (r16 == 0 && (wave & 1) == 0) a.Y_sf[slot * (a.n_out / 32) + cx / 32] = (uint8_t)code;
+            }
+          }
+      }
+    };
+    store(y[0], col);
+    if (two) store(y[1], a.I + col);
   } else {
     // GEMM2: columns n0 + wave*32 + n*16 + r16
 #pragma unroll
@@ -495,10 +509,11 @@ hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
   a.pts = p.per_token_scale;
   a.bias = p.fc1_bias;
   a.K = p.H;
-  a.rows_per_expert = 2 * p.I;
-  a.I = p.I;
+  const int IP = gemm1_pairs(p);
+  a.rows_per_expert = 2 * IP;
+  a.I = IP;
   a.n_out = p.I;
-  a.n_tiles = p.I / 64;
+  a.n_tiles = IP / 64;
   a.total_tiles = a.m_tiles * a.n_tiles;
   a.act = p.act;
   a.fc2_scale = p.fc2_input_scale;

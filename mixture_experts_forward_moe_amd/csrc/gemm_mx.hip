@@ -279,11 +279,30 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
     // give columns +r16, tiles 1 / 3 columns 16 + r16
     const int col0 = nb * 128 + 32 * wave;
     uint8_t* Yq = reinterpret_cast<uint8_t*>(a.Y);
+    // gated: one output block per gate / up pair block; ReLU^2 (non-gated):
+    // the two row blocks are output blocks col0 and a.I + col0
+    const bool two = a.act.kind == ACT_RELU2;
+    // one 32-column MXFP8 block of a row: its scale from the 16-lane max,
+    // element pairs stored as 16-bit words
+    auto put = [&](const float (&y)[2], int row, int cb) {
+      const float am = warp_max16(fmaxf(fabsf(y[0]), fabsf(y[1])));
+      const uint32_t code = mx_scale_code(am, 8);
+      const float y0n = __shfl_xor(y[0], 1), y1n = __shfl_xor(y[1], 1);
+      if (row < valid) {
+        const int64_t slot = slot0 + row;
+        if ((r16 & 1) == 0) {
+          *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + cb + r16) = (uint16_t)f32x2_to_e4m3x2_mx(y[0], y0n, code);
+          *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + cb + 16 + r16) =
+              (uint16_t)f32x2_to_e4m3x2_mx(y[1], y1n, code);
+        }
+        if (r16 == 0) a.Y_sf[slot * (a.n_out / 32) + cb / 32] = (uint8_t)code;
+      }
+    };
 #pragma unroll
     for (int m = 0; m < MTV; m++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        float y[2];
+        float y[2], yu[2];
 #pragma unroll
         for (int n = 0; n < 2; n++) {
           float g = acc[m][n][i] * alpha;
@@ -293,22 +312,17 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
             u = u + a.bias[(int64_t)e * 2 * a.I + a.I + col0 + 16 * n + r16];
           }
           // y1 is rounded once to bf16; requantisation starts from that value
-          y[n] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
-        }
-        const float am = warp_max16(fmaxf(fabsf(y[0]), fabsf(y[1])));
-        const uint32_t code = mx_scale_code(am, 8);
-        const float y0n = __shfl_xor(y[0], 1), y1n = __shfl_xor(y[1], 1);
-        const int row = 16 * m + 4 * q + i;
-        if (row < valid) {
-          const int64_t slot = slot0 + row;
-          if ((r16 & 1) == 0) {
-            *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + col0 + r16) =
-                (uint16_t)f32x2_to_e4m3x2_mx(y[0], y0n, code);
-            *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + col0 + 16 + r16) =
-                (uint16_t)f32x2_to_e4m3x2_mx(y[1], y1n, code);
+          if (two) {
+            y[n] = bf16_to_f32(f32_to_bf16(relu2_f32(g)));
+            yu[n] = bf16_to_f32(f32_to_bf16(relu2_f32(u)));
+          } else {
+            y[n] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
+            yu[n] = 0.0f;
           }
-          if (r16 == 0) a.Y_sf[slot * (a.n_out / 32) + col0 / 32] = (uint8_t)code;
         }
+        const int row = 16 * m + 4 * q + i;
+        put(y, row, col0);
+        if (two) put(yu, row, a.I + col0);
       }
   } else {
 #pragma unroll
@@ -420,7 +434,8 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
 bool mx_supported1(const Gemm1Params& p) {
   const int64_t stride = p.x_row_stride ? p.x_row_stride : p.H;
   if ((int64_t)p.plan->M * stride >= (1ll << 32) || (int64_t)2 * p.I * (p.H / 2) >= (1ll << 32)) return false;
-  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == XM && p.H % (NR * XK) == 0 && p.I % 128 == 0 &&
+  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == XM && p.H % (NR * XK) == 0 &&
+         gemm1_pairs(p) % 128 == 0 &&
          stride % 16 == 0 && aligned4(p.x_sf) && aligned4(p.w1_sf) && aligned4(p.y1_sf) &&
          ((uintptr_t)p.y1 & 1) == 0;
 }
@@ -443,10 +458,11 @@ hipError_t launch_gemm1_mx(const Gemm1Params& p, hipStream_t stream) {
   a.alpha_up = p.w1_alpha_up;
   a.bias = p.fc1_bias;
   a.K = p.H;
-  a.rows_per_expert = 2 * p.I;
-  a.I = p.I;
+  const int IP = gemm1_pairs(p);
+  a.rows_per_expert = 2 * IP;
+  a.I = IP;
   a.n_out = p.I;
-  a.n_blocks = p.I / 128;
+  a.n_blocks = IP / 128;
   a.act = p.act;
   a.Y = p.y1;
   a.Y_sf = p.y1_sf;

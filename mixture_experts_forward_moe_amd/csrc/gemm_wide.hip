@@ -280,7 +280,10 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
 #pragma unroll
     for (int n = 0; n < 2; n++) {
       const int col = nb * 128 + 32 * wave + 16 * n + r16;  // y1 column
-      float y[MTV][4];
+      // gated: one output per gate / up pair; ReLU^2 (non-gated): the two
+      // rows of a pair are outputs col and a.I + col
+      const bool two = a.act.kind == ACT_RELU2;
+      uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
 #pragma unroll
       for (int m = 0; m < MTV; m++)
 #pragma unroll
@@ -291,16 +294,16 @@ DEV void wide_body(const WArgs& a, uint8_t* smem, int e, int slot0, int valid, i
             g = g + a.bias[(int64_t)e * 2 * a.I + col];
             u = u + a.bias[(int64_t)e * 2 * a.I + a.I + col];
           }
-          // y1 is rounded once to bf16; requantisation starts from that value
-          y[m][i] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
-        }
-      uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
-#pragma unroll
-      for (int m = 0; m < MTV; m++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
           const int row = 16 * m + 4 * q + i;
-          if (row < valid) Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(y[m][i]);
+          // y1 is rounded once to bf16
+          if (row < valid) {
+            if (two) {
+              Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(relu2_f32(g));
+              Y[(int64_t)(slot0 + row) * a.n_out + a.I + col] = f32_to_bf16(relu2_f32(u));
+            } else {
+              Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(gated_act_f32(g, u, a.act));
+            }
+          }
         }
     }
   } else {
@@ -407,7 +410,7 @@ hipError_t launch(const WArgs& a, int max_tiles, hipStream_t s) {
 // blocks, and every activation / weight byte offset inside 32 bits
 bool wide_supported1(const Gemm1Params& p) {
   const int64_t stride = p.x_row_stride ? p.x_row_stride : p.H;
-  return p.mode == MOE_QUANT_W4A16 && p.plan->tile == WM && p.H % GK == 0 && p.I % 128 == 0 &&
+  return p.mode == MOE_QUANT_W4A16 && p.plan->tile == WM && p.H % GK == 0 && gemm1_pairs(p) % 128 == 0 &&
          (int64_t)p.plan->M * stride * 2 < (1ll << 32) && (int64_t)2 * p.I * (p.H / 2) < (1ll << 32);
 }
 bool wide_supported2(const Gemm2Params& p) {
@@ -426,10 +429,11 @@ hipError_t launch_gemm1_wide(const Gemm1Params& p, hipStream_t stream) {
   a.alpha_up = p.w1_alpha_up;
   a.bias = p.fc1_bias;
   a.K = p.H;
-  a.rows_per_expert = 2 * p.I;
-  a.I = p.I;
+  const int IP = gemm1_pairs(p);
+  a.rows_per_expert = 2 * IP;
+  a.I = IP;
   a.n_out = p.I;
-  a.n_blocks = p.I / 128;
+  a.n_blocks = IP / 128;
   a.act = p.act;
   a.Y = p.y1;
   return launch<1, false>(a, p.plan->max_tiles, stream);

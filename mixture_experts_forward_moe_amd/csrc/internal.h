@@ -52,6 +52,10 @@ struct Gemm2Params {
   uint16_t* out;
 };
 hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream);
+// W1 row pairs per expert that GEMM1 walks: gate / up pairs (I), or for the
+// non-gated ReLU^2 rows j and I/2 + j of its I rows, whose outputs are
+// y1 columns j and I/2 + j
+inline int gemm1_pairs(const Gemm1Params& p) { return p.act.kind == ACT_RELU2 ? p.I / 2 : p.I; }
 hipError_t launch_gemm2(const Gemm2Params& p, hipStream_t stream);
 
 // wide-tile kernels for 128-slot tiles (prefill-sized batches, W4A16 / W4A4)

@@ -172,8 +172,15 @@ __global__ __launch_bounds__(ST_THREADS) void gemm1_stream_kernel(const StreamAr
           gs = gs + a.bias[(int64_t)e * 2 * a.I + col];
           us = us + a.bias[(int64_t)e * 2 * a.I + a.I + col];
         }
-        const float y = gated_act_f32(gs, us, a.act);
-        if (row < valid) a.Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(y);
+        if (a.act.kind == ACT_RELU2) {  // non-gated: both rows are outputs
+          if (row < valid) {
+            a.Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(relu2_f32(gs));
+            a.Y[(int64_t)(slot0 + row) * a.n_out + a.I + col] = f32_to_bf16(relu2_f32(us));
+          }
+        } else {
+          const float y = gated_act_f32(gs, us, a.act);
+          if (row < valid) a.Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(y);
+        }
       }
     }
     __syncthreads();
@@ -279,8 +286,9 @@ hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream) {
   a.alpha_up = p.w1_alpha_up;
   a.bias = p.fc1_bias;
   a.K = p.H;
-  a.rows_per_expert = 2 * p.I;
-  a.I = p.I;
+  const int IP = gemm1_pairs(p);
+  a.rows_per_expert = 2 * IP;
+  a.I = IP;
   a.n_out = p.I;
   a.p2e = p.plan->permuted_to_expanded;
   a.tile_expert = p.plan->tile_to_expert;
@@ -292,7 +300,7 @@ hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream) {
   a.Y = reinterpret_cast<uint16_t*>(p.y1);
   const int P = tile_stride(p.plan);
   if (P == 0) return hipSuccess;
-  gemm1_stream_kernel<<<dim3(p.I / 16, P), ST_THREADS, 0, stream>>>(a);
+  gemm1_stream_kernel<<<dim3(IP / 16, P), ST_THREADS, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -104,7 +104,10 @@ def test_activation_argument_checks():
     F = FAKE
     g = lambda act, a=1.0, b=0.0, lim=moe.FLT_MAX, sb=0.0, slb=0.0, pts=None: L.moe_grouped_gemm1_act(
         0, F, None, 0, p, F, F, F, None, 256, 512, act, a, b, lim, sb, slb, None, pts, None, F, None, None)
-    assert g(moe.ACT_RELU2) == UNSUPPORTED                         # non-gated GEMM1 is not built
+    assert g(moe.ACT_RELU2, a=1.702) == INVALID                    # ReLU^2 takes no SwiGLU parameters
+    assert g(moe.ACT_RELU2, sb=0.5) == INVALID                     # ... nor SiTU ones
+    assert L.moe_grouped_gemm1_act(0, F, None, 0, p, F, F, F, F, 256, 512, moe.ACT_RELU2, 1.0, 0.0, moe.FLT_MAX,
+                                   0.0, 0.0, None, None, None, F, None, None) == INVALID  # no up half to scale
     assert g(7) == INVALID                                         # unknown activation
     assert g(moe.ACT_GEGLU_TANH, a=1.702) == INVALID               # GeGLU takes no SwiGLU parameters
     assert g(moe.ACT_GEGLU_TANH, lim=7.0) == INVALID
@@ -118,11 +121,11 @@ def test_activation_argument_checks():
     assert g(moe.ACT_SWIGLU, lim=0.0) == INVALID
     assert g(moe.ACT_SWIGLU, pts=F) == INVALID                     # per-token scales are W4A4 only
     # the forward checks the same rules before it enqueues anything
-    o = moe.make_opts(activation=moe.ACT_RELU2)
+    o = moe.make_opts(activation=7)
     o.workspace = 0x10000
     o.workspace_bytes = 1 << 30
     args = (F, None, F, F, F, F, F, F, F, F, 8, 2, 8, 0, 0, F, 16, 256, 512, ctypes.byref(o), None)
-    assert L.moe_forward(*args) == UNSUPPORTED
+    assert L.moe_forward(*args) == INVALID
     o.activation = moe.ACT_GEGLU_TANH
     o.swiglu_limit = 7.0
     assert L.moe_forward(*args) == INVALID

@@ -37,6 +37,13 @@ CASES = {
     "w4a4_situ": (oracle.W4A4, dict(M=40, H=256, I=256, E=8, El=8, k=2, seed=57, situ_beta=0.1)),
     "mx_geglu": (oracle.MXFP8_MXFP4, dict(M=450, H=512, I=512, E=8, El=6, k=3, seed=58, offset=1,
                                           router_bias_std=0.7, activation=oracle.ACT_GEGLU_TANH)),
+    # the non-gated ReLU^2 (W1 with I rows) through every GEMM1 kernel
+    "w4a16_relu2": (oracle.W4A16, dict(M=60, H=512, I=512, E=8, El=8, k=3, seed=62, activation=oracle.ACT_RELU2)),
+    "w4a16_relu2_tall": (oracle.W4A16, dict(M=500, H=512, I=512, E=8, El=8, k=2, seed=63, router_bias_std=0.5,
+                                            activation=oracle.ACT_RELU2)),
+    "w4a4_relu2": (oracle.W4A4, dict(M=40, H=256, I=256, E=8, El=8, k=2, seed=64, activation=oracle.ACT_RELU2)),
+    "mx_relu2": (oracle.MXFP8_MXFP4, dict(M=450, H=512, I=512, E=8, El=6, k=3, seed=65, offset=1,
+                                          router_bias_std=0.7, activation=oracle.ACT_RELU2)),
 }
 
 _cache = {}
@@ -238,6 +245,9 @@ def decode_case(case):
         p.fc2_bias = rng.normal(0.0, 0.05, (p.num_local_experts, p.H)).astype(np.float32)
         p.routed_scaling_factor = 2.5
         return p
+    elif case == "relu2":
+        wl = synth.small_workload(oracle.W4A16, 9, 2048, 1024, 64, 16, 6, 66, offset=8, activation=oracle.ACT_RELU2)
+        raw = synth.make_raw(wl)
     elif case == "geglu":
         wl = synth.small_workload(oracle.W4A16, 9, 2048, 1536, 64, 16, 6, 59, offset=8,
                                   activation=oracle.ACT_GEGLU_TANH)
@@ -253,7 +263,7 @@ def decode_case(case):
 
 
 @pytest.mark.parametrize("case", ["no_local_routes", "hot_experts", "one_token", "offset_swiglu", "geglu", "situ",
-                                  "scaled"])
+                                  "scaled", "relu2"])
 def test_decode_path_edge_cases(case):
     """Decode-sized batches (tile 16) through the single-launch path: no
     local route at all, experts with several tiles and a ragged last tile,
