@@ -159,6 +159,23 @@ DEV float gated_act_f32(float g, float u, const GateAct& p) {
   return swiglu_f32(g, u, p.alpha, p.beta, p.limit);
 }
 
+// gated_act_f32 with the kind fixed at compile time (AK = ACT_SWIGLU,
+// ACT_GEGLU_TANH or ACT_SITU): for epilogues unrolled over many elements,
+// where carrying every kind's code per element would bloat them.
+template <int AK>
+DEV float gated_act_k(float g, float u, const GateAct& p) {
+  if constexpr (AK == ACT_GEGLU_TANH) {
+    const float z = 0.7978845608028654f * (g + 0.044715f * g * g * g);
+    return 0.5f * g * (1.0f + tanhf(z)) * u;
+  } else if constexpr (AK == ACT_SITU) {
+    const float gate = p.situ_beta * tanhf(g / p.situ_beta) / (1.0f + expf(-g));
+    const float up = p.situ_lin > 0.0f ? p.situ_lin * tanhf(u / p.situ_lin) : u;
+    return gate * up;
+  } else {
+    return swiglu_f32(g, u, p.alpha, p.beta, p.limit);
+  }
+}
+
 // ReLU^2 of one FC1 row (activation_type Relu2, non-gated): max(h, 0)^2.
 DEV float relu2_f32(float h) {
   const float r = fmaxf(h, 0.0f);

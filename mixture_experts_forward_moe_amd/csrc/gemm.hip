@@ -355,7 +355,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
           y[1][m][i] = 0.0f;
         }
       }
-    auto store = [&](const float (&ys)[MT][4], const int cx) {
+    auto store = [&](const float (&ys)[MT][4], const int cx) __attribute__((always_inline)) {
       if constexpr (MODE == M_W4A16) {
         uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
 #pragma unroll

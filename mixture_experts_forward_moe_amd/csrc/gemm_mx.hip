@@ -45,6 +45,7 @@
 //    of every tile, so an expert's weights are read by one XCD.  The grid is
 //    capped and loops over the work.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -96,7 +97,25 @@ struct XArgs {
 // physical 16-byte chunk of logical chunk c in an activation row of the stage
 DEV int xsw(int slot) { return (slot >> 1) & 7; }
 
-template <int GEMM, bool ATOMIC, int MTV>
+// One 32-column MXFP8 block of a y1 row (columns cb + r16 and cb + 16 + r16
+// in this lane): the E8M0 scale from the block's 16-lane max, element pairs
+// stored as 16-bit words, the scale by lane 0.
+DEV void mx_put_block(const XArgs& a, uint8_t* Yq, float y0, float y1, int row, int valid, int slot0, int cb,
+                      int r16) {
+  const float am = warp_max16(fmaxf(fabsf(y0), fabsf(y1)));
+  const uint32_t code = mx_scale_code(am, 8);
+  const float y0n = __shfl_xor(y0, 1), y1n = __shfl_xor(y1, 1);
+  if (row < valid) {
+    const int64_t slot = slot0 + row;
+    if ((r16 & 1) == 0) {
+      *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + cb + r16) = (uint16_t)f32x2_to_e4m3x2_mx(y0, y0n, code);
+      *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + cb + 16 + r16) = (uint16_t)f32x2_to_e4m3x2_mx(y1, y1n, code);
+    }
+    if (r16 == 0) a.Y_sf[slot * (a.n_out / 32) + cb / 32] = (uint8_t)code;
+  }
+}
+
+template <int GEMM, bool ATOMIC, int MTV, int AK, bool BIAS2>
 DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int nb) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
@@ -281,48 +300,33 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
     uint8_t* Yq = reinterpret_cast<uint8_t*>(a.Y);
     // gated: one output block per gate / up pair block; ReLU^2 (non-gated):
     // the two row blocks are output blocks col0 and a.I + col0
-    const bool two = a.act.kind == ACT_RELU2;
-    // one 32-column MXFP8 block of a row: its scale from the 16-lane max,
-    // element pairs stored as 16-bit words
-    auto put = [&](const float (&y)[2], int row, int cb) {
-      const float am = warp_max16(fmaxf(fabsf(y[0]), fabsf(y[1])));
-      const uint32_t code = mx_scale_code(am, 8);
-      const float y0n = __shfl_xor(y[0], 1), y1n = __shfl_xor(y[1], 1);
-      if (row < valid) {
-        const int64_t slot = slot0 + row;
-        if ((r16 & 1) == 0) {
-          *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + cb + r16) = (uint16_t)f32x2_to_e4m3x2_mx(y[0], y0n, code);
-          *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + cb + 16 + r16) =
-              (uint16_t)f32x2_to_e4m3x2_mx(y[1], y1n, code);
-        }
-        if (r16 == 0) a.Y_sf[slot * (a.n_out / 32) + cb / 32] = (uint8_t)code;
-      }
-    };
+    // (AK is the template form of a.act.kind: each body holds the code of one
+    // activation, so the unrolled epilogue stays small)
 #pragma unroll
     for (int m = 0; m < MTV; m++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        float y[2], yu[2];
+        float g[2], u[2];
 #pragma unroll
         for (int n = 0; n < 2; n++) {
-          float g = acc[m][n][i] * alpha;
-          float u = acc[m][n + 2][i] * alpha_u;
+          g[n] = acc[m][n][i] * alpha;
+          u[n] = acc[m][n + 2][i] * alpha_u;
           if (a.bias) {
-            g = g + a.bias[(int64_t)e * 2 * a.I + col0 + 16 * n + r16];
-            u = u + a.bias[(int64_t)e * 2 * a.I + a.I + col0 + 16 * n + r16];
-          }
-          // y1 is rounded once to bf16; requantisation starts from that value
-          if (two) {
-            y[n] = bf16_to_f32(f32_to_bf16(relu2_f32(g)));
-            yu[n] = bf16_to_f32(f32_to_bf16(relu2_f32(u)));
-          } else {
-            y[n] = bf16_to_f32(f32_to_bf16(gated_act_f32(g, u, a.act)));
-            yu[n] = 0.0f;
+            g[n] = g[n] + a.bias[(int64_t)e * 2 * a.I + col0 + 16 * n + r16];
+            u[n] = u[n] + a.bias[(int64_t)e * 2 * a.I + a.I + col0 + 16 * n + r16];
           }
         }
         const int row = 16 * m + 4 * q + i;
-        put(y, row, col0);
-        if (two) put(yu, row, a.I + col0);
+        // y1 is rounded once to bf16; requantisation starts from that value
+        if constexpr (AK == ACT_RELU2) {
+          mx_put_block(a, Yq, bf16_to_f32(f32_to_bf16(relu2_f32(g[0]))), bf16_to_f32(f32_to_bf16(relu2_f32(g[1]))),
+                       row, valid, slot0, col0, r16);
+          mx_put_block(a, Yq, bf16_to_f32(f32_to_bf16(relu2_f32(u[0]))), bf16_to_f32(f32_to_bf16(relu2_f32(u[1]))),
+                       row, valid, slot0, a.I + col0, r16);
+        } else {
+          mx_put_block(a, Yq, bf16_to_f32(f32_to_bf16(gated_act_k<AK>(g[0], u[0], a.act))),
+                       bf16_to_f32(f32_to_bf16(gated_act_k<AK>(g[1], u[1], a.act))), row, valid, slot0, col0, r16);
+        }
       }
   } else {
 #pragma unroll
@@ -337,7 +341,7 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
             for (int n = 0; n < 4; n++) {
               const int col = nb * XN + 64 * wave + 16 * n + r16;
               float v = acc[m][n][i] * alpha;
-              if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
+              if constexpr (BIAS2) v = v + a.bias[(int64_t)e * a.n_out + col];
               Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(v);
             }
           }
@@ -348,7 +352,7 @@ DEV void mx_body(const XArgs& a, uint8_t* smem, int e, int slot0, int valid, int
           for (int n = 0; n < 4; n++) {
             const int col = nb * XN + 64 * wave + 16 * n + r16;
             float v = acc[m][n][i] * alpha;
-            if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
+            if constexpr (BIAS2) v = v + a.bias[(int64_t)e * a.n_out + col];
             const float y2 = bf16_to_f32(f32_to_bf16(v));
             const float c = __fmul_rn(wf, y2);
             const float cn = __shfl_xor(c, 1);
@@ -392,15 +396,33 @@ __global__ __launch_bounds__(XT, 1) void mx_gemm_kernel(const XArgs a) {
     const int e = __builtin_amdgcn_readfirstlane(a.tile_expert[pt]);
     const int slot0 = pt * XM;
     const int valid = __builtin_amdgcn_readfirstlane(min(XM, a.tile_limit[pt] - slot0));
+    // one body per (used height, activation); GEMM2 has no activation but a
+    // body with and one without its bias (BIAS2; GEMM1 checks its bias at run time)
+    const int ak = GEMM == 1 ? a.act.kind : ACT_SWIGLU;
+    auto run = [&](auto h) {
+      constexpr int H = decltype(h)::value;
+      if constexpr (GEMM == 1) {
+        switch (ak) {
+          case ACT_GEGLU_TANH: mx_body<GEMM, ATOMIC, H, ACT_GEGLU_TANH, false>(a, smem, e, slot0, valid, nb); break;
+          case ACT_SITU: mx_body<GEMM, ATOMIC, H, ACT_SITU, false>(a, smem, e, slot0, valid, nb); break;
+          case ACT_RELU2: mx_body<GEMM, ATOMIC, H, ACT_RELU2, false>(a, smem, e, slot0, valid, nb); break;
+          default: mx_body<GEMM, ATOMIC, H, ACT_SWIGLU, false>(a, smem, e, slot0, valid, nb); break;
+        }
+      } else if (a.bias) {
+        mx_body<GEMM, ATOMIC, H, ACT_SWIGLU, true>(a, smem, e, slot0, valid, nb);
+      } else {
+        mx_body<GEMM, ATOMIC, H, ACT_SWIGLU, false>(a, smem, e, slot0, valid, nb);
+      }
+    };
     switch ((valid + 15) >> 4) {
-      case 1: mx_body<GEMM, ATOMIC, 1>(a, smem, e, slot0, valid, nb); break;
-      case 2: mx_body<GEMM, ATOMIC, 2>(a, smem, e, slot0, valid, nb); break;
-      case 3: mx_body<GEMM, ATOMIC, 3>(a, smem, e, slot0, valid, nb); break;
-      case 4: mx_body<GEMM, ATOMIC, 4>(a, smem, e, slot0, valid, nb); break;
-      case 5: mx_body<GEMM, ATOMIC, 5>(a, smem, e, slot0, valid, nb); break;
-      case 6: mx_body<GEMM, ATOMIC, 6>(a, smem, e, slot0, valid, nb); break;
-      case 7: mx_body<GEMM, ATOMIC, 7>(a, smem, e, slot0, valid, nb); break;
-      default: mx_body<GEMM, ATOMIC, 8>(a, smem, e, slot0, valid, nb); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      case 4: run(std::integral_constant<int, 4>{}); break;
+      case 5: run(std::integral_constant<int, 5>{}); break;
+      case 6: run(std::integral_constant<int, 6>{}); break;
+      case 7: run(std::integral_constant<int, 7>{}); break;
+      default: run(std::integral_constant<int, 8>{}); break;
     }
     // the next item's tile lookup and prologue reuse the LDS
     __syncthreads();
