@@ -30,6 +30,8 @@
 // (v_cvt_f32_fp8): about one VALU instruction per weight element and
 // activation row, where a decode to scaled bf16 costs two.  The 16 chunk
 // lanes of a row reduce with a fixed xor tree, so results are reproducible.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -366,7 +368,7 @@ DEV void stream_pairs(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t u
 // Workgroup (bx, y) computes y1 columns 32 bx .. 32 bx + 31 (16 per pass)
 // of tiles y, y + gridDim.y, ...; wavefront w, lane (rr, ch) owns column
 // 32 bx + 16 p + 4 w + rr of pass p.
-template <int D, int NP>
+template <int D, int NP, int AK>
 __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
   const int R = a.M * a.top_k;
@@ -434,11 +436,11 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
             us = us + a.fc1_bias[(int64_t)e * 2 * a.ip + a.ip + col + 16 * p];
           }
           uint16_t* yrow = a.y1 + (int64_t)(slot0 + r0) * a.I;
-          if (a.act.kind == ACT_RELU2) {  // non-gated: both rows are outputs
+          if constexpr (AK == ACT_RELU2) {  // non-gated: both rows are outputs
             yrow[col + 16 * p] = f32_to_bf16(relu2_f32(gs));
             yrow[a.ip + col + 16 * p] = f32_to_bf16(relu2_f32(us));
           } else {
-            yrow[col + 16 * p] = f32_to_bf16(gated_act_f32(gs, us, a.act));
+            yrow[col + 16 * p] = f32_to_bf16(gated_act_k<AK>(gs, us, a.act));
           }
         }
       }
@@ -741,9 +743,21 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int ns1 = a.H / 512;
   const dim3 g1(a.ip / (16 * G1_NP), P), g2(a.H / 64, P);
   if (p.mark) p.mark(p.mark_ctx, 1);
-  if (ns1 % G1_D == 0) dec_gemm1_kernel<G1_D, G1_NP><<<g1, DEC_THREADS, lds1, stream>>>(a);
-  else if (ns1 % 2 == 0) dec_gemm1_kernel<2, G1_NP><<<g1, DEC_THREADS, lds1, stream>>>(a);
-  else dec_gemm1_kernel<1, G1_NP><<<g1, DEC_THREADS, lds1, stream>>>(a);
+  // one kernel per activation: the epilogue holds only its own code
+  auto go = [&](auto dk, auto ak) {
+    dec_gemm1_kernel<decltype(dk)::value, G1_NP, decltype(ak)::value><<<g1, DEC_THREADS, lds1, stream>>>(a);
+  };
+  auto by_act = [&](auto dk) {
+    switch (a.act.kind) {
+      case ACT_GEGLU_TANH: go(dk, std::integral_constant<int, ACT_GEGLU_TANH>{}); break;
+      case ACT_SITU: go(dk, std::integral_constant<int, ACT_SITU>{}); break;
+      case ACT_RELU2: go(dk, std::integral_constant<int, ACT_RELU2>{}); break;
+      default: go(dk, std::integral_constant<int, ACT_SWIGLU>{}); break;
+    }
+  };
+  if (ns1 % G1_D == 0) by_act(std::integral_constant<int, G1_D>{});
+  else if (ns1 % 2 == 0) by_act(std::integral_constant<int, 2>{});
+  else by_act(std::integral_constant<int, 1>{});
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.mark) p.mark(p.mark_ctx, 2);
