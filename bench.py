@@ -145,7 +145,7 @@ def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False):
     import mixture_experts_forward_moe_amd as moe
     g = GpuInputs(wl, copies)
     H, I, E = wl.H, wl.I, wl.num_local_experts
-    tile = moe.default_tile(wl.M, wl.top_k, E, wl.mode)
+    tile = moe.default_tile(wl.M, wl.top_k, wl.num_experts, E, wl.mode)
     ws = torch.zeros(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.M, H), dtype=torch.int16, device="cuda")
     skw = _scale_kw(g, scaled)
@@ -193,7 +193,7 @@ def time_phases(wl, steps: int, warmup: int, copies: int, scaled: bool = False):
     import mixture_experts_forward_moe_amd as moe
     g = GpuInputs(wl, copies)
     H, I, E = wl.H, wl.I, wl.num_local_experts
-    tile = moe.default_tile(wl.M, wl.top_k, E, wl.mode)
+    tile = moe.default_tile(wl.M, wl.top_k, wl.num_experts, E, wl.mode)
     ws = torch.zeros(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.M, H), dtype=torch.int16, device="cuda")
     nev = moe.NUM_PHASE_EVENTS

@@ -117,25 +117,47 @@ typedef struct moe_plan {
 /* Static text for a status code. */
 const char* moe_status_string(moe_status_t status);
 
-/* Slot capacity of a plan (see moe_plan_t). */
+/* Slot capacity of a plan: the number of permuted rows the grouped GEMMs
+ * are sized for, the counterpart of get_max_num_permuted_tokens(num_tokens,
+ * top_k, num_local_experts, route_tile) in "vllm.models.flint.ops.moe_cute"
+ * (grouped_moe; the page names the function and does not print it).  It is
+ * round_up(M*top_k + min(E_l, M*top_k)*(tile-1), tile): every local route
+ * plus at most tile-1 padding rows for each expert that has a route, which
+ * bounds the padded total for any routing without reading it back.
+ * Returns 0 for M < 0, top_k < 1, num_local_experts < 1 or tile < 1. */
 int64_t moe_route_slots(int M, int top_k, int num_local_experts, int tile);
 
-/* Bytes of device workspace a plan needs, 256-byte aligned pieces. */
+/* Bytes of device workspace a plan needs, 256-byte aligned pieces: the
+ * counterpart of allocate_moe_sort_buffers in "vllm.models.flint.ops.moe_cute"
+ * (grouped_moe), caller-owned as the routing workspace of
+ * "flashinfer.fused_moe.alphamoe_nvfp4_routed_moe" (Parameters).  0 for
+ * arguments moe_plan_init would reject. */
 size_t moe_plan_workspace_size(int M, int top_k, int num_local_experts, int tile);
 
 /* Carve a plan out of `workspace` (device memory, >= moe_plan_workspace_size
  * bytes, 256-byte aligned).  Host-only; enqueues nothing.  tile must be a
  * power of two in [16, 256]; M >= 0, top_k in [1, 64], num_local_experts in
- * [1, 4096]. */
+ * [1, 512] (MOE_ERR_INVALID_ARGUMENT, or MOE_ERR_UNSUPPORTED for a tile or
+ * expert count outside these limits; MOE_ERR_WORKSPACE for a missing,
+ * unaligned or short workspace). */
 moe_status_t moe_plan_init(moe_plan_t* plan, void* workspace, size_t workspace_bytes, int M, int top_k,
                            int num_local_experts, int tile);
 
 /* moe_sort: build the routing plan from topk_ids (device int32 [M, top_k],
- * global expert ids).  Routes with local_expert_offset <= id <
- * local_expert_offset + num_local_experts belong to this GPU; others are
- * dropped.  Requires local_expert_offset >= 0 and local_expert_offset +
- * num_local_experts <= num_experts; M, top_k and num_local_experts must
- * equal the plan's.  Bit-exact and reproducible. */
+ * global expert ids): the moe_sort step of "vllm.models.flint.ops.moe_cute"
+ * (grouped_moe: tile_idx_to_expert_idx, tile_idx_to_mn_limit,
+ * expanded_idx_to_permuted_idx, permuted_idx_to_expanded_idx,
+ * total_num_padded_tokens), restricted to this GPU's experts as
+ * num_local_experts / local_expert_offset of
+ * "flashinfer.fused_moe.cute_dsl_fused_moe" (Parameters) state.  Routes with
+ * local_expert_offset <= id < local_expert_offset + num_local_experts belong
+ * to this GPU; others are dropped.  The order inside an expert is ascending
+ * route index (the pages' order is atomic arrival; this one is stable, so
+ * the plan is bit-exact and reproducible), and SPAN gives the same plan as
+ * SINGLE through the contiguous per-workgroup route spans of FlashInfer pull
+ * request 4440 (description, item 2).  Requires local_expert_offset >= 0 and
+ * local_expert_offset + num_local_experts <= num_experts; M, top_k and
+ * num_local_experts must equal the plan's (MOE_ERR_INVALID_ARGUMENT). */
 moe_status_t moe_sort(const int32_t* topk_ids, int M, int top_k, int num_experts, int num_local_experts,
                       int local_expert_offset, moe_route_order_t route_order, const moe_plan_t* plan,
                       moe_stream_t stream);
@@ -267,8 +289,8 @@ typedef struct moe_opts {
   int route_order;               /* moe_route_order_t, default AUTO */
   int tile;                      /* route tile; 0 = moe_default_tile() */
   int64_t x_row_stride;          /* 0 = contiguous rows */
-  void* workspace;               /* device, >= moe_workspace_size() bytes, 256-byte aligned,
-                                    zero-filled before its first moe_forward (see below) */
+  void* workspace;               /* device, >= moe_workspace_size() bytes, 256-byte aligned;
+                                    any initial contents (see moe_workspace_size) */
   size_t workspace_bytes;
   void** phase_events;           /* optional: MOE_NUM_PHASE_EVENTS hipEvent_t recorded on the
                                     stream before sort, after sort, after GEMM1, after GEMM2,
@@ -287,20 +309,36 @@ typedef struct moe_opts {
 
 void moe_opts_init(moe_opts_t* opts);
 
-/* The route tile moe_forward uses when opts->tile == 0. */
-int moe_default_tile(int M, int top_k, int num_local_experts, moe_quant_mode_t mode);
+/* The route tile moe_forward uses when opts->tile == 0 (the route_tile of
+ * "vllm.models.flint.ops.moe_cute", grouped_moe, which the page's caller
+ * picks per batch).  It estimates the routes per local expert as
+ * M * top_k / num_experts (the local share of the routes spread over the
+ * local experts) and returns 16 up to 16 routes, 32 up to 48, 64 up to 96,
+ * else 128. */
+int moe_default_tile(int M, int top_k, int num_experts, int num_local_experts, moe_quant_mode_t mode);
 
-/* Device workspace of moe_forward: a block of MOE_WORKSPACE_COUNTER_BYTES
- * of counters, the plan, y1 (+ y1_sf) and, in deterministic mode or on the
- * decode path, y2.  The counter block must be zero before the first
- * moe_forward that uses the workspace (zero-fill the allocation, or its
- * first MOE_WORKSPACE_COUNTER_BYTES, once); every call leaves it zero
- * again, and no other entry point writes it.  The counters coordinate the
- * workgroups of the decode path's single launch, so two moe_forward calls
- * in flight at once must not share a workspace. */
-#define MOE_WORKSPACE_COUNTER_BYTES 401664
+/* Bytes of device workspace moe_forward needs: the caller-owned buffers of
+ * "flashinfer.fused_moe.alphamoe_nvfp4_routed_moe" (Parameters: routing
+ * workspace, permuted intermediates) in one allocation.  It holds, in
+ * 256-byte aligned pieces: a counter block of the decode path (one done
+ * count per 64 output columns, cleared by the forward's own GEMM1 launch),
+ * the routing plan (moe_forward_plan), y1 (+ y1_sf) and, in deterministic
+ * mode or on the decode path, y2.  The workspace needs no initial contents;
+ * every piece is written before it is read within one call.  Two
+ * moe_forward calls in flight at once must not share a workspace.  Returns
+ * 0 for arguments moe_forward would reject as invalid. */
 size_t moe_workspace_size(int M, int H, int I, int top_k, int num_local_experts, int tile,
                           moe_quant_mode_t mode, int finalize_mode);
+
+/* The routing plan inside a moe_forward workspace: after a moe_forward on
+ * that workspace has run with the same M, top_k, num_local_experts and tile
+ * (the tile it used: opts->tile, or moe_default_tile), `plan` points at the
+ * plan that forward built and used (every array of moe_plan_t, as moe_sort
+ * writes them), also on the decode path, which builds it inside GEMM1.
+ * Host-only, enqueues nothing.  MOE_ERR_WORKSPACE if the workspace is NULL
+ * or too small for the plan; otherwise as moe_plan_init. */
+moe_status_t moe_forward_plan(moe_plan_t* plan, void* workspace, size_t workspace_bytes, int M, int top_k,
+                              int num_local_experts, int tile);
 
 /* moe_forward: the whole pass, argument order as the
  * cute_dsl_fused_moe signature (x, x_sf, token_selected_experts,

@@ -17,14 +17,13 @@ W4A16, W4A4, MXFP8_MXFP4 = 0, 1, 2
 FINALIZE_DETERMINISTIC, FINALIZE_ATOMIC = 0, 1
 ROUTE_ORDER_AUTO, ROUTE_ORDER_SINGLE, ROUTE_ORDER_SPAN = 0, 1, 2
 NUM_PHASE_EVENTS = 5
-WORKSPACE_COUNTER_BYTES = 401664  # the forward workspace's counter block (MOE_WORKSPACE_COUNTER_BYTES)
 FLT_MAX = 3.4028234663852886e38
 ACT_SWIGLU, ACT_GEGLU_TANH, ACT_RELU2 = 0, 1, 2   # moe_activation_t (SiTU: ACT_SWIGLU with situ_beta > 0)
 
 EXPORTS = [
     "moe_status_string", "moe_route_slots", "moe_plan_workspace_size", "moe_plan_init", "moe_sort",
     "moe_grouped_gemm1_swiglu", "moe_grouped_gemm1_act", "moe_grouped_gemm2", "moe_grouped_gemm2_bias", "moe_finalize", "moe_opts_init", "moe_default_tile",
-    "moe_workspace_size", "moe_forward", "moe_nvfp4_global_scale", "moe_quantize_nvfp4", "moe_quantize_mx",
+    "moe_workspace_size", "moe_forward_plan", "moe_forward", "moe_nvfp4_global_scale", "moe_quantize_nvfp4", "moe_quantize_mx",
 ]
 
 
@@ -81,8 +80,9 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_gemm2": ([I, P, P, P, P, P, P, I, I, P, P, F, P, P], I),
             "moe_finalize": ([P, P, P, I, F, I, P, P], I),
             "moe_opts_init": ([P], None),
-            "moe_default_tile": ([I, I, I, I], I),
+            "moe_default_tile": ([I, I, I, I, I], I),
             "moe_workspace_size": ([I, I, I, I, I, I, I, I], SZ),
+            "moe_forward_plan": ([P, P, SZ, I, I, I, I], I),
             "moe_forward": ([P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I, I, P, P], I),
             "moe_nvfp4_global_scale": ([P, I64, I64, P, P], I),
             "moe_quantize_nvfp4": ([P, I64, I64, I64, P, P, P, P], I),
@@ -122,8 +122,8 @@ def route_slots(M: int, top_k: int, num_local_experts: int, tile: int) -> int:
     return lib().moe_route_slots(M, top_k, num_local_experts, tile)
 
 
-def default_tile(M: int, top_k: int, num_local_experts: int, mode: int) -> int:
-    return lib().moe_default_tile(M, top_k, num_local_experts, mode)
+def default_tile(M: int, top_k: int, num_experts: int, num_local_experts: int, mode: int) -> int:
+    return lib().moe_default_tile(M, top_k, num_experts, num_local_experts, mode)
 
 
 def workspace_size(M, H, I, top_k, num_local_experts, tile, mode, finalize_mode=FINALIZE_DETERMINISTIC) -> int:
@@ -133,23 +133,31 @@ def workspace_size(M, H, I, top_k, num_local_experts, tile, mode, finalize_mode=
 def _alloc(nbytes: int, device):
     import torch
     # 256-byte alignment: torch's caching allocator aligns blocks to 512 bytes.
-    # Zero-filled: a forward workspace's counter block starts at zero.
-    t = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    # No initial contents are needed: every piece is written before it is read.
+    t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
     assert t.data_ptr() % 256 == 0
     return t
 
 
 class MoePlan:
-    """A routing plan with its device workspace (torch-owned)."""
+    """A routing plan with its device workspace (torch-owned).  With
+    `forward_workspace`, a view of the plan a moe_forward built in that
+    workspace (moe_forward_plan) instead of a workspace of its own."""
 
-    def __init__(self, M: int, top_k: int, num_local_experts: int, tile: int, device="cuda"):
-        n = lib().moe_plan_workspace_size(M, top_k, num_local_experts, tile)
-        if n == 0:
-            raise MoeError(1, "moe_plan_workspace_size")
-        self.workspace = _alloc(n, device)
+    def __init__(self, M: int, top_k: int, num_local_experts: int, tile: int, device="cuda",
+                 forward_workspace=None):
         self.c = Plan()
-        _check(lib().moe_plan_init(ctypes.byref(self.c), _ptr(self.workspace), n, M, top_k, num_local_experts, tile),
-               "moe_plan_init")
+        if forward_workspace is not None:
+            self.workspace = forward_workspace
+            _check(lib().moe_forward_plan(ctypes.byref(self.c), _ptr(forward_workspace), forward_workspace.numel(),
+                                          M, top_k, num_local_experts, tile), "moe_forward_plan")
+        else:
+            n = lib().moe_plan_workspace_size(M, top_k, num_local_experts, tile)
+            if n == 0:
+                raise MoeError(1, "moe_plan_workspace_size")
+            self.workspace = _alloc(n, device)
+            _check(lib().moe_plan_init(ctypes.byref(self.c), _ptr(self.workspace), n, M, top_k, num_local_experts,
+                                       tile), "moe_plan_init")
         self.M, self.top_k, self.num_local_experts, self.tile = M, top_k, num_local_experts, tile
         self.route_slots = self.c.route_slots
         self.max_tiles = self.c.max_tiles
@@ -274,7 +282,7 @@ def moe_forward(x, x_sf, topk_ids, topk_weights, w1, w1_sf, w1_alpha, w2, w2_sf,
     from `workspace`, or allocated here (outside the library) when None."""
     M = topk_ids.shape[0]
     if opts is None:
-        tile = kw.pop("tile", 0) or default_tile(M, top_k, num_local_experts, quant_mode)
+        tile = kw.pop("tile", 0) or default_tile(M, top_k, num_experts, num_local_experts, quant_mode)
         fm = kw.get("finalize_mode", FINALIZE_DETERMINISTIC)
         if workspace is None:
             workspace = _alloc(workspace_size(M, H, I, top_k, num_local_experts, tile, quant_mode, fm), x.device)

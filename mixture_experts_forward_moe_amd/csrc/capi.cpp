@@ -291,28 +291,38 @@ void moe_opts_init(moe_opts_t* o) {
   o->x_row_stride = 0;
 }
 
-int moe_default_tile(int M, int top_k, int num_local_experts, moe_quant_mode_t mode) {
+int moe_default_tile(int M, int top_k, int num_experts, int num_local_experts, moe_quant_mode_t mode) {
   (void)mode;
-  const int64_t per_expert = (int64_t)M * top_k / (num_local_experts > 0 ? num_local_experts : 1);
+  // routes per local expert, expected: of the M * top_k routes, those that
+  // land on this GPU's num_local_experts of num_experts
+  const int El = num_local_experts > 0 ? num_local_experts : 1;
+  const int E = num_experts > El ? num_experts : El;
+  const double per_expert = (double)M * top_k / E;
   if (per_expert <= 16) return 16;
-  if (per_expert <= 64) return 32;
-  if (per_expert <= 256) return 64;
+  if (per_expert <= 48) return 32;
+  if (per_expert <= 96) return 64;
   return 128;
 }
-
-static_assert(MOE_WORKSPACE_COUNTER_BYTES == DEC_COUNTER_BYTES, "counter block size in moe.h");
 
 size_t moe_workspace_size(int M, int H, int I, int top_k, int num_local_experts, int tile, moe_quant_mode_t mode,
                           int finalize_mode) {
   if (!plan_args_ok(M, top_k, num_local_experts, tile) || !mode_ok(mode) || H <= 0 || I <= 0) return 0;
   PlanLayout L = plan_layout(M, top_k, num_local_experts, tile);
-  // the decode path's counter block first, at a place no shape moves
+  // the decode path's counter block first, then the plan (moe_forward_plan)
   size_t total = DEC_COUNTER_BYTES + L.total;
   total = align256(total + y1_bytes(mode, L.slots, I));
   total = align256(total + y1_sf_bytes(mode, L.slots, I));
   const bool dec = tile == 16 && decode_supported(mode, M, top_k, num_local_experts, H, I);
   if (finalize_mode == MOE_FINALIZE_DETERMINISTIC || dec) total = align256(total + (size_t)L.slots * H * 2);
   return total;
+}
+
+moe_status_t moe_forward_plan(moe_plan_t* plan, void* workspace, size_t workspace_bytes, int M, int top_k,
+                              int num_local_experts, int tile) {
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < DEC_COUNTER_BYTES) return MOE_ERR_WORKSPACE;
+  return moe_plan_init(plan, (uint8_t*)workspace + DEC_COUNTER_BYTES, workspace_bytes - DEC_COUNTER_BYTES, M, top_k,
+                       num_local_experts, tile);
 }
 
 namespace {
@@ -351,7 +361,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
                opts->situ_linear_beta, &act);
   if (s != MOE_OK) return s;
   if (act.kind == ACT_RELU2 && opts->w1_alpha_up) return MOE_ERR_INVALID_ARGUMENT;  // no up half
-  const int tile = opts->tile ? opts->tile : moe_default_tile(M, top_k, num_local_experts, quant_mode);
+  const int tile = opts->tile ? opts->tile : moe_default_tile(M, top_k, num_experts, num_local_experts, quant_mode);
   if (!pow2_in(tile, 16, 256)) return MOE_ERR_UNSUPPORTED;
   const size_t need = moe_workspace_size(M, H, I, top_k, num_local_experts, tile, quant_mode, opts->finalize_mode);
   if (!opts->workspace || opts->workspace_bytes < need || ((uintptr_t)opts->workspace & 255) != 0)
@@ -360,10 +370,9 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   moe_plan_t plan;
   PlanLayout L = plan_layout(M, top_k, num_local_experts, tile);
   int* counters = (int*)opts->workspace;
-  uint8_t* base = (uint8_t*)opts->workspace + DEC_COUNTER_BYTES;
-  s = moe_plan_init(&plan, base, L.total, M, top_k, num_local_experts, tile);
+  s = moe_forward_plan(&plan, opts->workspace, opts->workspace_bytes, M, top_k, num_local_experts, tile);
   if (s != MOE_OK) return s;
-  base += L.total;
+  uint8_t* base = (uint8_t*)opts->workspace + DEC_COUNTER_BYTES + L.total;
   void* y1 = base;
   base += align256(y1_bytes(quant_mode, L.slots, I));
   uint8_t* y1_sf = (quant_mode == MOE_QUANT_W4A16) ? NULL : base;

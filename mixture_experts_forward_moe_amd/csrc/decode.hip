@@ -363,6 +363,9 @@ DEV void stream_pairs(const uint8_t* W, const uint8_t* Wsf, int64_t g, int64_t u
     dot_chunk2<1>(bg[d], bu[d], xs, 0, ch + 16 * (NS - D + d), &ag[NP - 1], &au[NP - 1]);
 }
 
+// GEMM2's done count of column group c (64 columns of H)
+DEV int* done_count(const DecArgs& a, int c) { return a.counters + DEC_CTR_SLOT * c; }
+
 // ---------------------------------------------------------------- GEMM1
 
 // Workgroup (bx, y) computes y1 columns 32 bx .. 32 bx + 31 (16 per pass)
@@ -385,6 +388,11 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
   const int xs_word = (3 * a.El + 1 + DEC_THREADS / 64 + R + DEC_T + 3) & ~3;
   uint32_t* xs = dsm + xs_word;  // [H/2]
 
+  // GEMM2 of this forward counts finished workgroups per column group from
+  // zero; it runs after this launch in the same stream
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int c = threadIdx.x; c < a.H / 64; c += DEC_THREADS)
+      __hip_atomic_store(done_count(a, c), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int nt = plan_counts(a, P);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rr = lane >> 4, ch = lane & 15;
@@ -521,10 +529,10 @@ DEV void stream_rows16(const uint8_t* W, const uint8_t* Wsf, int64_t row0, int K
 // other workgroups compute.  Those go through device-scope stores (they
 // bypass the CU's L1 and stay coherent across the L2s of all XCDs); each
 // workgroup waits for its stores to complete and then bumps its column
-// group's count, and the workgroup that brings the count to the number of
-// workgroups per column group finalizes those columns for every token and
-// clears the count for the next call.  Nothing waits on anything, so there
-// is no forward-progress condition.  The stores write through to memory, so
+// group's count (cleared by GEMM1 of the same forward), and the workgroup
+// that brings the count to the number of workgroups per column group
+// finalizes those columns for every token.  Nothing waits on anything, so
+// there is no forward-progress condition.  The stores write through to memory, so
 // a workgroup gathers a row's 64 outputs in LDS and stores them as one
 // 128-byte line from 32 lanes.
 
@@ -605,8 +613,6 @@ DEV void finalize_cols(const DecArgs& a, int c0, const int (*fs)[DEC_FJ], const 
   }
 }
 
-DEV int* done_count(const DecArgs& a, int c) { return a.counters + DEC_CTR_SLOT * (1 + DEC_MAX_TILES + c); }
-
 constexpr int DEC_YMAX = 4;  // u32x4 per thread for one y1 row: I <= 8192
 
 // Workgroup (bx, y): y2 columns 64 bx .. 64 bx + 63 of tiles y, y +
@@ -679,10 +685,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm2_kernel(const DecArgs a)
   const int old = publish_bump(done_count(a, blockIdx.x));
   if (tid == 0) last = (old == (int)gridDim.y - 1);
   __syncthreads();
-  if (last) {
-    finalize_cols(a, c0, fs, fw);
-    if (tid == 0) __hip_atomic_store(done_count(a, blockIdx.x), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (last) finalize_cols(a, c0, fs, fw);
 }
 
 // ---------------------------------------------------------------- host side

@@ -93,7 +93,7 @@ struct DecodeParams {
   GateAct act;
   uint16_t* y1;
   uint16_t* y2;
-  int* counters;  // the decode counter block (DEC_COUNTER_BYTES), zero between calls
+  int* counters;  // the decode counter block (DEC_COUNTER_BYTES); GEMM1 clears it for GEMM2
   const float* topk_weights;
   float routed_scaling_factor;
   int accumulate;
@@ -103,14 +103,13 @@ struct DecodeParams {
   void* mark_ctx;
 };
 // Decode path limits.  Its counter block sits at the head of the forward
-// workspace: a head slot (finalized column groups, stalled waits), one
-// ready count per plan tile and one done count per 64 columns of H, each
-// in a 256-byte slot of its own.
+// workspace: one done count per 64 columns of H, each in a 256-byte slot of
+// its own (atomics on one line queue at the memory side).  GEMM1 clears the
+// counts GEMM2 will use, so the block needs no initial contents.
 constexpr int DEC_MAX_ROUTES = 1024;
-constexpr int DEC_MAX_TILES = (DEC_MAX_ROUTES + MAX_LOCAL_EXPERTS * 15) / 16;  // 16-slot tiles
-constexpr int DEC_MAX_COL_GROUPS = 1024;                                       // H <= 65536
-constexpr int DEC_CTR_SLOT = 64;                                               // ints per counter slot
-constexpr size_t DEC_COUNTER_BYTES = sizeof(int) * DEC_CTR_SLOT * (1 + DEC_MAX_TILES + DEC_MAX_COL_GROUPS);
+constexpr int DEC_MAX_COL_GROUPS = 1024;  // H <= 65536
+constexpr int DEC_CTR_SLOT = 64;          // ints per counter slot
+constexpr size_t DEC_COUNTER_BYTES = sizeof(int) * DEC_CTR_SLOT * DEC_MAX_COL_GROUPS;
 bool decode_supported(int mode, int M, int top_k, int El, int H, int I);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 

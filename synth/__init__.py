@@ -144,9 +144,9 @@ WORKLOADS = {
                              num_local_experts=32, top_k=8, seed=1),
     "w4a16_prefill": Workload("w4a16_prefill", W4A16, M=4096, H=6144, I=2048, num_experts=256,
                               num_local_experts=32, top_k=8, seed=2, router_bias_std=0.5,
-                              swiglu_limit=7.0, sample_tokens=64),
+                              swiglu_limit=7.0),
     "w4a4_nvfp4": Workload("w4a4_nvfp4", W4A4, M=512, H=4096, I=1536, num_experts=128,
-                           num_local_experts=128, top_k=8, seed=3, sample_tokens=64),
+                           num_local_experts=128, top_k=8, seed=3),
     "mxfp8_mxfp4_large": Workload("mxfp8_mxfp4_large", MXFP8_MXFP4, M=65536, H=6144, I=2048,
                                   num_experts=256, num_local_experts=32, top_k=8, seed=4,
                                   sample_tokens=1024),

@@ -155,7 +155,21 @@ def test_workspace_size_grows_with_mode():
     b = moe.workspace_size(16, 256, 512, 2, 8, 16, 0, 1)   # atomic: no y2
     c = moe.workspace_size(16, 256, 512, 2, 8, 16, 1, 0)   # NVFP4 y1 is smaller than bf16
     assert a > b > 0 and a > c > 0
-    assert moe.default_tile(8, 8, 32, 0) == 16
+
+
+def test_default_tile_counts_local_routes():
+    """The tile rule estimates routes per local expert from the local share of
+    the routes (M * top_k * E_l / E over E_l experts), not from all routes."""
+    assert moe.default_tile(8, 8, 256, 32, 0) == 16          # decode: 0.25 routes per expert
+    assert moe.default_tile(16, 2, 8, 8, 0) == 16            # tiny: 4
+    assert moe.default_tile(512, 8, 128, 128, 1) == 32       # W4A4: 32
+    assert moe.default_tile(4096, 8, 256, 32, 0) == 128      # prefill: 128
+    assert moe.default_tile(65536, 8, 256, 32, 2) == 128     # MX large batch: 2048
+    # the same batch over 8x the global experts puts 1/8 of the routes here
+    assert moe.default_tile(1024, 8, 64, 8, 0) == 128        # 128 per expert
+    assert moe.default_tile(1024, 8, 512, 8, 0) == 16        # 16 per expert
+    assert moe.default_tile(1024, 8, 256, 8, 0) == 32        # 32 per expert
+    assert moe.default_tile(1024, 8, 128, 8, 0) == 64        # 64 per expert
 
 
 def test_header_constants_match_binding():
@@ -163,10 +177,28 @@ def test_header_constants_match_binding():
     import re
     text = open(HEADER).read()
     consts = dict(re.findall(r"#define\s+(MOE_\w+)\s+(\d+)", text))
-    assert int(consts["MOE_WORKSPACE_COUNTER_BYTES"]) == moe.WORKSPACE_COUNTER_BYTES
     assert int(consts["MOE_NUM_PHASE_EVENTS"]) == moe.NUM_PHASE_EVENTS
-    # the counter block leads every forward workspace
-    assert moe.workspace_size(8, 1024, 512, 8, 32, 16, 0) > moe.WORKSPACE_COUNTER_BYTES
+
+
+def test_forward_plan_view():
+    """moe_forward_plan carves the plan at a fixed place inside a forward
+    workspace: after the counter block, inside the workspace, with the
+    capacity of a plan of the same shape, and rejects a short workspace."""
+    L = moe.lib()
+    for (M, H, I, k, El, tile, mode) in [(8, 6144, 2048, 8, 32, 16, 0), (4096, 6144, 2048, 8, 32, 128, 0),
+                                         (16, 256, 512, 2, 8, 16, 1), (512, 4096, 1536, 8, 128, 32, 2)]:
+        n = moe.workspace_size(M, H, I, k, El, tile, mode)
+        pn = L.moe_plan_workspace_size(M, k, El, tile)
+        p = moe.Plan()
+        assert L.moe_forward_plan(ctypes.byref(p), FAKE, n, M, k, El, tile) == OK
+        base = FAKE.value
+        assert p.expanded_to_permuted % 256 == 0 and p.expanded_to_permuted > base
+        assert p.scratch - base < n and p.route_slots == moe.route_slots(M, k, El, tile)
+        assert p.expanded_to_permuted - base + pn <= n
+        assert L.moe_forward_plan(ctypes.byref(p), FAKE, p.expanded_to_permuted - base + pn - 1, M, k, El,
+                                  tile) == WORKSPACE
+        assert L.moe_forward_plan(ctypes.byref(p), None, n, M, k, El, tile) == WORKSPACE
+        assert L.moe_forward_plan(None, FAKE, n, M, k, El, tile) == INVALID
 
 
 def test_forward_accepts_the_workspace_it_asks_for():

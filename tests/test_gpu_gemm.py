@@ -217,7 +217,7 @@ def test_row_strided_x():
 
 
 def takes_decode_path(p, tile=16):
-    """The single-launch decode path keeps y2 in its workspace in either
+    """The two-launch decode path keeps y2 in its workspace in either
     finalize mode; the tiled path keeps it in deterministic mode only."""
     import mixture_experts_forward_moe_amd as moe
     args = (p.M, p.H, p.I, p.top_k, p.num_local_experts, tile, p.mode)
@@ -265,7 +265,7 @@ def decode_case(case):
 @pytest.mark.parametrize("case", ["no_local_routes", "hot_experts", "one_token", "offset_swiglu", "geglu", "situ",
                                   "scaled", "relu2"])
 def test_decode_path_edge_cases(case):
-    """Decode-sized batches (tile 16) through the single-launch path: no
+    """Decode-sized batches (tile 16) through the two-launch path: no
     local route at all, experts with several tiles and a ragged last tile,
     a single token, an expert window with a clamped SwiGLU."""
     import torch
@@ -295,10 +295,41 @@ def test_decode_path_edge_cases(case):
                     p.mode, f"decode {case} accumulate")
 
 
+DECODE_PLAN_CASES = ["w4a16_decode", "no_local_routes", "hot_experts", "one_token", "offset_swiglu", "relu2"]
+
+
+@pytest.mark.parametrize("case", DECODE_PLAN_CASES)
+@pytest.mark.parametrize("fill", [0xA5, 0xFF])
+def test_decode_forward_plan_bit_exact(case, fill):
+    """The routing plan the decode forward builds inside its GEMM1 launch and
+    leaves in its workspace (moe_forward_plan): all seven arrays bit for bit
+    against the oracle's plan at tile 16, on a workspace whose bytes all
+    start non-zero (the forward needs no zeroed counters), with the output
+    meeting the bar against the oracle."""
+    import torch
+
+    from gpu_util import DeviceProblem, assert_plan_equal, check_close, forward_in_workspace, host, say
+    say(f"decode forward plan {case} fill {fill:#x}")
+    if case == "w4a16_decode":
+        p = oracle.quantize_problem(synth.make_raw(synth.WORKLOADS[case]))
+    else:
+        p = decode_case(case)
+    assert takes_decode_path(p)
+    d = DeviceProblem(p)
+    out, plan = forward_in_workspace(d, 16, fill=fill)
+    torch.cuda.synchronize()
+    assert_plan_equal(plan, oracle.sort(p.topk_ids, p.num_local_experts, p.local_expert_offset, 16), case)
+    want = oracle.forward_tokens(p, np.arange(p.M))
+    if case == "no_local_routes":
+        assert np.all(host(out, np.uint16) == 0) and np.all(want == 0)
+    else:
+        check_close(host(out, np.uint16), want, p.mode, f"decode {case} on a {fill:#x}-filled workspace")
+
+
 def test_decode_path_workspace_reuse():
-    """One workspace through many calls: the decode launch's counters must
-    come back to zero after every call, whatever shape came before (a
-    tiled-path call in between included), and results stay bit-identical."""
+    """One workspace, first filled with non-zero bytes, through many calls of
+    different shapes (a tiled-path call in between included): results stay
+    bit-identical to calls on fresh workspaces."""
     import torch
 
     import mixture_experts_forward_moe_amd as moe
@@ -307,7 +338,7 @@ def test_decode_path_workspace_reuse():
     probs = [decode_case("offset_swiglu"), decode_case("hot_experts"), decode_case("one_token"),
              problem("w4a16_basic")]
     sizes = [moe.workspace_size(p.M, p.H, p.I, p.top_k, p.num_local_experts, 16, p.mode) for p in probs]
-    ws = torch.zeros(max(sizes), dtype=torch.uint8, device="cuda")
+    ws = torch.full((max(sizes),), 0x7F, dtype=torch.uint8, device="cuda")
     devs = [DeviceProblem(p) for p in probs]
     first = [d.forward(tile=16) for d in devs]  # fresh workspace each
     torch.cuda.synchronize()
@@ -316,8 +347,6 @@ def test_decode_path_workspace_reuse():
             out = devs[i].forward(tile=16, workspace=ws)
             torch.cuda.synchronize()
             assert torch.equal(out, first[i]), (rep, i)
-    counters = host(ws[:moe.WORKSPACE_COUNTER_BYTES].view(torch.int32))
-    assert np.all(counters == 0), np.nonzero(counters)
 
 
 def test_decode_sized_batch_with_unaligned_scales():
@@ -346,10 +375,10 @@ def test_decode_sized_batch_with_unaligned_scales():
 
 
 def test_decode_path_graph_replay():
-    """The single-launch decode path captured in a HIP graph: every replay,
+    """The two-launch decode path captured in a HIP graph: every replay,
     with eager calls on the same workspace in between, gives the eager
-    result bit for bit (the launch clears its own counters, so replays need
-    no fill nodes)."""
+    result bit for bit (GEMM1 clears GEMM2's counters, so replays need no
+    fill nodes)."""
     import torch
 
     import mixture_experts_forward_moe_amd as moe
