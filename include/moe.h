@@ -20,7 +20,8 @@
  *    allocates, frees or reads back device memory and never synchronises the
  *    host; every call only enqueues work on `stream` (a hipStream_t, NULL
  *    for the default stream), so calls can be captured into a HIP graph.
- *  - The library has no mutable global state; concurrent calls on
+ *  - The library has no mutable global state apart from the scratch array
+ *    of moe_forward_noalloc; concurrent calls of the other entry points on
  *    different streams are safe when their buffers do not overlap.
  *  - Arguments are checked on the host before anything is enqueued.  On a
  *    non-MOE_OK return nothing has been enqueued, except MOE_ERR_DEVICE,
@@ -50,7 +51,8 @@ typedef enum {
   MOE_ERR_INVALID_ARGUMENT = 1, /* NULL where required, non-NULL where forbidden, bad sizes */
   MOE_ERR_UNSUPPORTED = 2,      /* a valid request this build does not implement (the message names it) */
   MOE_ERR_WORKSPACE = 3,        /* workspace missing or smaller than moe_workspace_size() */
-  MOE_ERR_DEVICE = 4            /* a HIP launch failed */
+  MOE_ERR_DEVICE = 4,           /* a HIP launch failed */
+  MOE_ERR_SCRATCH_TOO_SMALL = 5 /* moe_forward_noalloc: the pass needs more than MOE_NOALLOC_SCRATCH_BYTES */
 } moe_status_t;
 
 /* Quantisation modes ("quant_mode" of cute_dsl_fused_moe, Parameters):
@@ -361,6 +363,28 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
                          const uint8_t* w2_sf, const float* w2_alpha, int num_experts, int top_k,
                          int num_local_experts, int local_expert_offset, moe_quant_mode_t quant_mode,
                          uint16_t* out, int M, int H, int I, const moe_opts_t* opts, moe_stream_t stream);
+
+/* moe_forward_noalloc: moe_forward for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments and results as moe_forward, but
+ * the workspace is a fixed array inside the library: opts->workspace must
+ * be NULL and opts->workspace_bytes 0 (else MOE_ERR_INVALID_ARGUMENT).
+ * The array holds MOE_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU the
+ * library runs on, from the first call on that device until the process
+ * ends; a pass whose moe_workspace_size() (at opts->tile, or
+ * moe_default_tile) is larger returns MOE_ERR_SCRATCH_TOO_SMALL and enqueues
+ * nothing.  The call allocates and frees nothing (its first call on a
+ * device looks up the array's address there, a host-side query).  All calls
+ * on one GPU share that GPU's array: two calls whose work overlaps on the
+ * device (different streams, or host threads without ordering) race on it
+ * and give undefined results; calls on one stream are ordered and safe. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_forward_noalloc(const void* x, const uint8_t* x_sf, const int32_t* topk_ids,
+                                 const float* topk_weights, const uint8_t* w1, const uint8_t* w1_sf,
+                                 const float* w1_alpha, const uint8_t* w2, const uint8_t* w2_sf,
+                                 const float* w2_alpha, int num_experts, int top_k, int num_local_experts,
+                                 int local_expert_offset, moe_quant_mode_t quant_mode, uint16_t* out, int M, int H,
+                                 int I, const moe_opts_t* opts, moe_stream_t stream);
 
 /* ---- Input preparation (model-load / activation quantisers) ----------- */
 

@@ -18,12 +18,13 @@ FINALIZE_DETERMINISTIC, FINALIZE_ATOMIC = 0, 1
 ROUTE_ORDER_AUTO, ROUTE_ORDER_SINGLE, ROUTE_ORDER_SPAN = 0, 1, 2
 NUM_PHASE_EVENTS = 5
 FLT_MAX = 3.4028234663852886e38
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 ACT_SWIGLU, ACT_GEGLU_TANH, ACT_RELU2 = 0, 1, 2   # moe_activation_t (SiTU: ACT_SWIGLU with situ_beta > 0)
 
 EXPORTS = [
     "moe_status_string", "moe_route_slots", "moe_plan_workspace_size", "moe_plan_init", "moe_sort",
     "moe_grouped_gemm1_swiglu", "moe_grouped_gemm1_act", "moe_grouped_gemm2", "moe_grouped_gemm2_bias", "moe_finalize", "moe_opts_init", "moe_default_tile",
-    "moe_workspace_size", "moe_forward_plan", "moe_forward", "moe_nvfp4_global_scale", "moe_quantize_nvfp4", "moe_quantize_mx",
+    "moe_workspace_size", "moe_forward_plan", "moe_forward", "moe_forward_noalloc", "moe_nvfp4_global_scale", "moe_quantize_nvfp4", "moe_quantize_mx",
 ]
 
 
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_size": ([I, I, I, I, I, I, I, I], SZ),
             "moe_forward_plan": ([P, P, SZ, I, I, I, I], I),
             "moe_forward": ([P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I, I, P, P], I),
+            "moe_forward_noalloc": ([P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I, I, P, P], I),
             "moe_nvfp4_global_scale": ([P, I64, I64, P, P], I),
             "moe_quantize_nvfp4": ([P, I64, I64, I64, P, P, P, P], I),
             "moe_quantize_mx": ([P, I64, I64, I, P, P, P], I),
@@ -291,6 +293,20 @@ def moe_forward(x, x_sf, topk_ids, topk_weights, w1, w1_sf, w1_alpha, w2, w2_sf,
                              _ptr(w1_alpha), _ptr(w2), _ptr(w2_sf), _ptr(w2_alpha), num_experts, top_k,
                              num_local_experts, local_expert_offset, quant_mode, _ptr(out), M, H, I,
                              ctypes.byref(opts), _stream(stream)), "moe_forward")
+    return out
+
+
+def moe_forward_noalloc(x, x_sf, topk_ids, topk_weights, w1, w1_sf, w1_alpha, w2, w2_sf, w2_alpha, num_experts: int,
+                        top_k: int, num_local_experts: int, local_expert_offset: int, quant_mode: int, out, H: int,
+                        I: int, stream=None, **kw):
+    """moe_forward with the library's own fixed scratch array as workspace
+    (nothing is allocated, here or in the library)."""
+    M = topk_ids.shape[0]
+    opts = make_opts(**kw)
+    _check(lib().moe_forward_noalloc(_ptr(x), _ptr(x_sf), _ptr(topk_ids), _ptr(topk_weights), _ptr(w1), _ptr(w1_sf),
+                                     _ptr(w1_alpha), _ptr(w2), _ptr(w2_sf), _ptr(w2_alpha), num_experts, top_k,
+                                     num_local_experts, local_expert_offset, quant_mode, _ptr(out), M, H, I,
+                                     ctypes.byref(opts), _stream(stream)), "moe_forward_noalloc")
     return out
 
 

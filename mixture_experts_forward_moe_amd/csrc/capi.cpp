@@ -114,6 +114,8 @@ const char* moe_status_string(moe_status_t s) {
                                      "tile a power of two in [16, 256]; at most 512 local experts)";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_DEVICE: return "HIP launch failed";
+    case MOE_ERR_SCRATCH_TOO_SMALL:
+      return "the pass needs more workspace than the no-allocation scratch array holds (MOE_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

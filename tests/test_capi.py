@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert moe.status_string(s)
 
 
@@ -148,6 +148,32 @@ def test_forward_argument_checks():
     assert L.moe_forward(*args(0, None)) == INVALID
     o.finalize_mode = 0
     assert L.moe_forward(F, None, F, F, F, F, F, F, F, F, 8, 2, 8, 0, 0, F, 16, 256, 512, None, None) == INVALID
+
+
+def test_forward_noalloc_host_checks():
+    """moe_forward_noalloc takes no workspace and refuses, before anything
+    is enqueued, a pass larger than its scratch array."""
+    L = moe.lib()
+    F = FAKE
+    o = moe.make_opts()
+    ws_opts = moe.make_opts()
+    ws_opts.workspace = 0x10000
+    ws_opts.workspace_bytes = 1 << 20
+    args = lambda opts, M=8, H=6144, I=2048, E=256, El=32, k=8: (
+        F, None, F, F, F, F, F, F, F, F, E, k, El, 0, 0, F, M, H, I, ctypes.byref(opts), None)
+    assert L.moe_forward_noalloc(*args(ws_opts)) == INVALID
+    assert L.moe_forward_noalloc(F, None, F, F, F, F, F, F, F, F, 256, 8, 32, 0, 0, F, 8, 6144, 2048, None,
+                                 None) == INVALID
+    # the prefill workload needs far more than 64 MiB of workspace
+    need = moe.workspace_size(4096, 6144, 2048, 8, 32, 128, 0)
+    assert need > moe.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(*args(o, M=4096)) == 5
+    assert "scratch" in moe.status_string(5)
+    # the decode workload fits
+    assert moe.workspace_size(8, 6144, 2048, 8, 32, 16, 0) <= moe.NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert moe.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_workspace_size_grows_with_mode():
