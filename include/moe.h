@@ -181,7 +181,10 @@ moe_status_t moe_sort(const int32_t* topk_ids, int M, int top_k, int num_experts
  * W4A16.  w1 packed E2M1 [E_l, 2I, H/2]; w1_sf E4M3 [E_l, 2I, H/16] (NVFP4)
  * or E8M0 [E_l, 2I, H/32] (MX); w1_alpha fp32 [E_l].  fc2_input_scale: a
  * device fp32 scalar, required in W4A4 and NULL otherwise.  H and I must be
- * multiples of 128 (of 256 in the MX mode), else MOE_ERR_UNSUPPORTED.
+ * multiples of the scale block (16 NVFP4, 32 MX; else
+ * MOE_ERR_INVALID_ARGUMENT) and of 32 (else MOE_ERR_UNSUPPORTED); tiles that
+ * N = I or K = H does not fill are masked, following the partial-N-tile
+ * support of FlashInfer pull request 4440 (description, item 1).
  * Padding rows of y1 are not written. */
 moe_status_t moe_grouped_gemm1_swiglu(moe_quant_mode_t mode, const void* x, const uint8_t* x_sf,
                                       int64_t x_row_stride, const moe_plan_t* plan, const uint8_t* w1,

@@ -59,12 +59,17 @@ bool plan_ok(const moe_plan_t* p) {
 
 bool mode_ok(int mode) { return mode == MOE_QUANT_W4A16 || mode == MOE_QUANT_W4A4 || mode == MOE_QUANT_MXFP8_MXFP4; }
 
-// shapes the kernels tile: H and I multiples of 128 (256 in the MX mode,
-// whose K step is 256)
-moe_status_t shape_check(int H, int I, int mode) {
+// shapes the kernels take: H and I multiples of the scale block (16 for
+// NVFP4, 32 for MX) are valid; the kernels need multiples of 32 (a packed
+// 16-byte load of codes spans 32 elements), with partial tiles masked.  The
+// non-gated ReLU^2 writes y1 columns [0, I/2) and [I/2, I) from separate row
+// blocks, so with MXFP8 y1 blocks of 32 it needs I a multiple of 64.
+moe_status_t shape_check(int H, int I, int mode, int activation = MOE_ACT_SWIGLU) {
   if (H <= 0 || I <= 0) return MOE_ERR_INVALID_ARGUMENT;
-  const int q = (mode == MOE_QUANT_MXFP8_MXFP4) ? 256 : 128;
-  if (H % q != 0 || I % q != 0) return MOE_ERR_UNSUPPORTED;
+  const int blk = (mode == MOE_QUANT_MXFP8_MXFP4) ? 32 : 16;
+  if (H % blk != 0 || I % blk != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 32 != 0 || I % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (activation == MOE_ACT_RELU2 && mode == MOE_QUANT_MXFP8_MXFP4 && I % 64 != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -110,8 +115,8 @@ const char* moe_status_string(moe_status_t s) {
   switch (s) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case MOE_ERR_UNSUPPORTED: return "unsupported shape or option (H and I must be multiples of 128, or of 256 in the MX mode; "
-                                     "tile a power of two in [16, 256]; at most 512 local experts)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or option (H and I must be multiples of 32, I of 64 for ReLU^2 "
+                                     "in the MX mode; tile a power of two in [16, 256]; at most 512 local experts)";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_DEVICE: return "HIP launch failed";
     case MOE_ERR_SCRATCH_TOO_SMALL:
@@ -182,7 +187,7 @@ moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const u
                                    const float* fc2_input_scale, const float* per_token_scale,
                                    const float* fc1_bias, void* y1, uint8_t* y1_sf, moe_stream_t stream) {
   if (!mode_ok(mode) || !plan_ok(plan)) return MOE_ERR_INVALID_ARGUMENT;
-  moe_status_t s = shape_check(H, I, mode);
+  moe_status_t s = shape_check(H, I, mode, activation);
   if (s != MOE_OK) return s;
   if (!w1 || !w1_sf || !w1_alpha || !y1) return MOE_ERR_INVALID_ARGUMENT;
   if (plan->M > 0 && !x) return MOE_ERR_INVALID_ARGUMENT;
@@ -348,7 +353,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   if (M < 0 || top_k < 1 || top_k > 64 || num_local_experts < 1) return MOE_ERR_INVALID_ARGUMENT;
   if (local_expert_offset < 0 || (int64_t)local_expert_offset + num_local_experts > num_experts)
     return MOE_ERR_INVALID_ARGUMENT;
-  moe_status_t s = shape_check(H, I, quant_mode);
+  moe_status_t s = shape_check(H, I, quant_mode, opts->activation);
   if (s != MOE_OK) return s;
   if (opts->finalize_mode != MOE_FINALIZE_DETERMINISTIC && opts->finalize_mode != MOE_FINALIZE_ATOMIC)
     return MOE_ERR_INVALID_ARGUMENT;

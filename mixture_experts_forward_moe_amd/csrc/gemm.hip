@@ -30,6 +30,11 @@
 //  - Tile order: a flat grid, remapped so that each XCD (blocks are dealt
 //    round-robin to the 8 XCDs) runs a contiguous range of tiles, slots
 //    fastest, so the weight tile of one expert is re-read from its L2.
+//  - Partial tiles (pull request 4440, description item 1: GEMM2 no longer
+//    needs N to divide the tile): N (2I gate/up rows, or H) and K (H or I)
+//    need only be multiples of 32.  Weight rows past N are clamped to the
+//    last row for loading and their outputs are not stored; K past the end
+//    of a step loads zero codes with zero scales, which add nothing.
 #include "device_common.h"
 #include "internal.h"
 
@@ -79,6 +84,15 @@ struct Cfg {
 
 // swizzled 16-byte chunk position inside an LDS tile of `rows` rows
 DEV int sw(int kc, int row, int rows) { return kc * rows + (row ^ (kc & 7)); }
+
+// the 8 block-scale bytes of one K step starting at p, of which only the
+// first n (>= 1) lie inside the row: the rest read as 0 (a zero scale)
+DEV uint2 load_scales8(const uint8_t* p, int n) {
+  if (n >= 8) return *reinterpret_cast<const uint2*>(p);
+  uint32_t w[2] = {0u, 0u};
+  for (int i = 0; i < n; i++) w[i >> 2] |= (uint32_t)p[i] << (8 * (i & 3));
+  return make_uint2(w[0], w[1]);
+}
 
 template <int MODE, int GEMM, int BM, bool ATOMIC>
 __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KArgs a) {
@@ -132,8 +146,11 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
   // weight rows of this tile
   const int j0 = n_tile * 64;   // GEMM1: gate/up column block
   const int n0 = n_tile * BN;   // GEMM2: output column block
+  // rows past the end of N (a partial last tile) load the last row; their
+  // outputs are never stored
   auto wrow = [&](int lr) -> int64_t {
-    int n = (GEMM == 1) ? (lr < 64 ? j0 + lr : a.I + j0 + lr - 64) : n0 + lr;
+    int n = (GEMM == 1) ? (lr < 64 ? min(j0 + lr, a.I - 1) : a.I + min(j0 + lr - 64, a.I - 1))
+                        : min(n0 + lr, a.n_out - 1);
     return (int64_t)e * a.rows_per_expert + n;
   };
   const int64_t w_row_bytes = a.K / 2;
@@ -159,7 +176,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
         int row = c / (BK / 32), part = c % (BK / 32);
         ra[i] = u32x4_t{0u, 0u, 0u, 0u};
         ra_sf[i] = 0u;
-        if (row < BM && row < valid) {
+        if (row < BM && row < valid && k0 + 32 * part < a.K) {
           int64_t src = row_src[row];
           const uint8_t* p = a.A + src * a.a_row_bytes + k0 / 2 + part * 16;
           ra[i] = *reinterpret_cast<const u32x4_t*>(p);
@@ -173,7 +190,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
         int c = tid + i * GEMM_THREADS;
         int row = c / AC, kc = c % AC;
         ra[i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < BM && row < valid) {
+        if (row < BM && row < valid && k0 + kc * (MODE == M_MX ? 16 : 8) < a.K) {
           int64_t src = row_src[row];
           const uint8_t* p = a.A + src * a.a_row_bytes + (MODE == M_MX ? k0 : k0 * 2) + kc * 16;
           ra[i] = *reinterpret_cast<const u32x4_t*>(p);
@@ -182,7 +199,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
       if constexpr (MODE == M_MX) {
         if (tid < BM) {
           rasf = make_uint2(0u, 0u);
-          if (tid < valid) rasf = *reinterpret_cast<const uint2*>(a.A_sf + row_src[tid] * a.a_sf_row + k0 / 32);
+          if (tid < valid) rasf = load_scales8(a.A_sf + row_src[tid] * a.a_sf_row + k0 / 32, (a.K - k0) / 32);
         }
       }
     }
@@ -192,11 +209,11 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
       int c = tid + i * GEMM_THREADS;
       int lr = c / BC, kc = c % BC;
       const uint8_t* p = a.W + wrow(lr) * w_row_bytes + k0 / 2 + kc * 16;
-      rb[i] = *reinterpret_cast<const u32x4_t*>(p);
+      rb[i] = (k0 + 32 * kc < a.K) ? *reinterpret_cast<const u32x4_t*>(p) : u32x4_t{0u, 0u, 0u, 0u};
     }
     if (tid < BN) {
-      const int sfk = (MODE == M_MX) ? k0 / 32 : k0 / 16;
-      rbsf = *reinterpret_cast<const uint2*>(a.W_sf + wrow(tid) * w_sf_row + sfk);
+      const int blk = (MODE == M_MX) ? 32 : 16;
+      rbsf = load_scales8(a.W_sf + wrow(tid) * w_sf_row + k0 / blk, (a.K - k0) / blk);
     }
   };
 
@@ -310,7 +327,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
   };
 
   // ---- main loop
-  const int KT = a.K / BK;
+  const int KT = (a.K + BK - 1) / BK;
   load_global(0);
   store_lds(0);
   __syncthreads();
@@ -325,7 +342,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
   const float alpha = a.alpha[e];
   if constexpr (GEMM == 1) {
     const float alpha_u = a.alpha_up ? a.alpha_up[e] : alpha;
-    const int col = j0 + wave * 16 + r16;  // output column of y1
+    const int col = j0 + wave * 16 + r16;  // output column of y1 (pair index)
+    const bool col_ok = col < a.I;           // false past the end of a partial tile
     // gated: one output per gate / up pair; ReLU^2 (non-gated): the two
     // rows of a pair are outputs col and a.I + col
     const bool two = a.act.kind == ACT_RELU2;
@@ -342,7 +360,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
           g = g * s;
           u = u * s;
         }
-        if (a.bias) {
+        if (a.bias && col_ok) {
           g = g + a.bias[(int64_t)e * 2 * a.I + col];
           u = u + a.bias[(int64_t)e * 2 * a.I + a.I + col];
         }
@@ -363,7 +381,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             int row = m * 16 + 4 * q + i;
-            if (row < valid) Y[(int64_t)(slot0 + row) * a.n_out + cx] = f32_to_bf16(ys[m][i]);
+            if (row < valid && col_ok) Y[(int64_t)(slot0 + row) * a.n_out + cx] = f32_to_bf16(ys[m][i]);
           }
       } else if constexpr (MODE == M_W4A4) {
         // NVFP4 with the global scale fc2_input_scale; a block is the 16
@@ -379,7 +397,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
             uint32_t sc = nvfp4_scale_code(bamax, gs);
             uint32_t code = nvfp4_elem_code(ys[m][i], e4m3_to_f32(sc), gs);
             uint32_t other = __shfl_xor(code, 1);
-            if (row < valid) {
+            if (row < valid && col_ok) {
               int64_t slot = slot0 + row;
               if ((r16 & 1) == 0) Yq[slot * (a.n_out / 2) + cx / 2] = (uint8_t)(code | (other << 4));
               if (r16 == 0) a.Y_sf[slot * (a.n_out / 16) + cx / 16] = (uint8_t)sc;
@@ -405,7 +423,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
             float am = fmaxf(red[wave][row], red[wave ^ 1][row]);
             uint32_t code = mx_scale_code(am, 8);
             uint32_t b = f32x2_to_e4m3x2_mx(ys[m][i], 0.0f, code) & 255u;
-            if (row < valid) {
+            if (row < valid && col_ok) {
               int64_t slot = slot0 + row;
               Yq[slot * a.n_out + cx] = (uint8_t)b;
               if (r16 == 0 && (wave & 1) == 0) a.Y_sf[slot * (a.n_out / 32) + cx / 32] = (uint8_t)code;
@@ -428,6 +446,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
 #pragma unroll
             for (int n = 0; n < 2; n++) {
               int col = n0 + wave * 32 + n * 16 + r16;
+              if (col >= a.n_out) continue;  // past the end of a partial tile
               float v = acc[m][n][i] * alpha;
               if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
               Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(v);
@@ -439,12 +458,13 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
 #pragma unroll
           for (int n = 0; n < 2; n++) {
             int col = n0 + wave * 32 + n * 16 + r16;
+            const bool ok = col < a.n_out;  // a partial tile ends at an even column
             float v = acc[m][n][i] * alpha;
-            if (a.bias) v = v + a.bias[(int64_t)e * a.n_out + col];
+            if (a.bias && ok) v = v + a.bias[(int64_t)e * a.n_out + col];
             float y2 = bf16_to_f32(f32_to_bf16(v));
             float c = __fmul_rn(wf, y2);
             float cn = __shfl_xor(c, 1);
-            if (route >= 0 && (r16 & 1) == 0) {
+            if (route >= 0 && ok && (r16 & 1) == 0) {
               int64_t t = route / a.top_k;
               bf16x2_t v = {(__bf16)c, (__bf16)cn};
               __builtin_amdgcn_global_atomic_fadd_v2bf16(
@@ -513,7 +533,7 @@ hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
   a.rows_per_expert = 2 * IP;
   a.I = IP;
   a.n_out = p.I;
-  a.n_tiles = IP / 64;
+  a.n_tiles = (IP + 63) / 64;
   a.total_tiles = a.m_tiles * a.n_tiles;
   a.act = p.act;
   a.fc2_scale = p.fc2_input_scale;
@@ -541,7 +561,7 @@ hipError_t launch_gemm2(const Gemm2Params& p, hipStream_t stream) {
   a.rows_per_expert = p.H;
   a.I = p.I;
   a.n_out = p.H;
-  a.n_tiles = p.H / BN;
+  a.n_tiles = (p.H + BN - 1) / BN;
   a.total_tiles = a.m_tiles * a.n_tiles;
   a.Y = p.y2;
   a.topk_w = p.topk_weights;

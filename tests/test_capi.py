@@ -86,8 +86,11 @@ def test_gemm_argument_checks():
     assert g1(0, F, F, 0, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, None, F, None, None) == INVALID
     assert g1(1, F, F, 0, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, None, F, F, None) == INVALID
     assert g1(2, F, F, 0, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, F, F, F, None) == INVALID
-    assert g1(0, F, None, 0, p, F, F, F, 200, 512, 1.0, 0.0, 1e30, None, F, None, None) == UNSUPPORTED
-    assert g1(0, F, None, 0, p, F, F, F, 256, 96, 1.0, 0.0, 1e30, None, F, None, None) == UNSUPPORTED
+    # H and I: multiples of the NVFP4 block (16) else invalid, of 32 else unsupported
+    assert g1(0, F, None, 0, p, F, F, F, 200, 512, 1.0, 0.0, 1e30, None, F, None, None) == INVALID
+    assert g1(0, F, None, 0, p, F, F, F, 208, 512, 1.0, 0.0, 1e30, None, F, None, None) == UNSUPPORTED
+    assert g1(0, F, None, 0, p, F, F, F, 256, 80, 1.0, 0.0, 1e30, None, F, None, None) == UNSUPPORTED
+    assert g1(2, F, F, 0, p, F, F, F, 256, 48, 1.0, 0.0, 1e30, None, F, F, None) == INVALID  # MX block 32
     assert g1(5, F, None, 0, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, None, F, None, None) == INVALID
     assert g1(0, F, None, 100, p, F, F, F, 256, 512, 1.0, 0.0, 1e30, None, F, None, None) == INVALID  # stride < H
     g2 = L.moe_grouped_gemm2
@@ -142,7 +145,8 @@ def test_forward_argument_checks():
     assert L.moe_forward(*args(0, None)) == WORKSPACE
     assert L.moe_forward(*args(0, F)) == INVALID
     assert L.moe_forward(*args(0, None, off=4)) == INVALID
-    assert L.moe_forward(*args(0, None, H=300)) == UNSUPPORTED
+    assert L.moe_forward(*args(0, None, H=300)) == INVALID       # not a multiple of the block
+    assert L.moe_forward(*args(0, None, H=304)) == UNSUPPORTED   # a multiple of 16, not of 32
     assert L.moe_forward(*args(1, F)) == INVALID                 # W4A4 needs fc2_input_scale
     o.finalize_mode = 3
     assert L.moe_forward(*args(0, None)) == INVALID

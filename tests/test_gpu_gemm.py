@@ -44,6 +44,18 @@ CASES = {
     "w4a4_relu2": (oracle.W4A4, dict(M=40, H=256, I=256, E=8, El=8, k=2, seed=64, activation=oracle.ACT_RELU2)),
     "mx_relu2": (oracle.MXFP8_MXFP4, dict(M=450, H=512, I=512, E=8, El=6, k=3, seed=65, offset=1,
                                           router_bias_std=0.7, activation=oracle.ACT_RELU2)),
+    # partial tiles (pull request 4440, description item 1 and its n = 192 test): H and I that do
+    # not fill the weight-row tiles (64 gate/up pairs, 128 GEMM2 columns) nor the K steps (128, or
+    # 256 in the MX mode), in every mode
+    "w4a16_partial": (oracle.W4A16, dict(M=70, H=192, I=320, E=8, El=6, k=3, seed=80, router_bias_std=0.5)),
+    "w4a4_partial": (oracle.W4A4, dict(M=70, H=192, I=320, E=8, El=6, k=3, seed=81, offset=2)),
+    "mx_partial": (oracle.MXFP8_MXFP4, dict(M=70, H=192, I=320, E=8, El=6, k=3, seed=82)),
+    "w4a16_geglu_partial": (oracle.W4A16, dict(M=300, H=320, I=96, E=4, El=4, k=2, seed=83,
+                                               activation=oracle.ACT_GEGLU_TANH)),
+    "w4a4_relu2_partial": (oracle.W4A4, dict(M=40, H=96, I=160, E=8, El=8, k=2, seed=84,
+                                             activation=oracle.ACT_RELU2)),
+    "mx_relu2_partial": (oracle.MXFP8_MXFP4, dict(M=300, H=192, I=320, E=8, El=6, k=3, seed=85, offset=1,
+                                                  router_bias_std=0.7, activation=oracle.ACT_RELU2)),
 }
 
 _cache = {}
@@ -132,7 +144,8 @@ def test_forward(name, tile):
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("name", ["w4a16_basic", "w4a16_stream_offset", "w4a4_offset", "mx_offset", "mx_tall"])
+@pytest.mark.parametrize("name", ["w4a16_basic", "w4a16_stream_offset", "w4a4_offset", "mx_offset", "mx_tall",
+                                  "w4a16_partial", "mx_partial"])
 def test_atomic_finalize_and_accumulate(name):
     import torch
 
@@ -158,7 +171,8 @@ def test_atomic_finalize_and_accumulate(name):
     check_close(host(out, np.uint16), want_acc, p.mode, f"{name} atomic accumulate")
 
 
-SCALED = ["w4a16_basic", "w4a16_wide", "w4a16_stream", "w4a4_offset", "w4a4_tall", "mx_tall"]
+SCALED = ["w4a16_basic", "w4a16_wide", "w4a16_stream", "w4a4_offset", "w4a4_tall", "mx_tall", "w4a16_partial",
+          "w4a4_partial", "mx_partial"]
 
 
 def scaled_problem(name):
