@@ -6,10 +6,16 @@ batch of seeded synthetic inputs already resident in HBM.  The headline
 workload is W4A16 decode (M=8 tokens, hidden 6144, inter 2048, 256 experts
 of which 32 are local, top_k 8), HBM-bound on weight bytes; the W4A16
 prefill workload (M=4096, biased router, SwiGLU limit 7), MFMA-bound, is
-reported alongside in the same line, and so are the W4A4 (M=512) and
-MXFP8 x MXFP4 (M=65536) parity configurations.  Weights, activations and routing are
-rotated over several resident copies so that no step finds the previous
-steps' weights in the 256 MB MALL.
+reported alongside in the same line, and so are the W4A4 (M=512, with a
+calibrated fc2_input_scale) and MXFP8 x MXFP4 (M=65536) configurations.
+Weights, activations and routing are rotated over several resident copies
+so that no step finds the previous steps' weights in the 256 MB MALL (the
+"cold" figure, the metric); the "warm" figure replays one copy.
+
+Also in the line: per-forward latency percentiles, the measured streaming
+copy bandwidth as a second roofline denominator, the routing-locality
+report of the large-batch plan (distinct 2 MiB pages of x per GEMM1 tile)
+and the CPU oracle timed on the host cores.
 
 Prints ONE JSON line (rank 0, N=1).
 """
@@ -36,13 +42,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def pct(v):
+    """median, p10, p90 of a list of times (ms)"""
+    a = np.asarray(v, np.float64)
+    return {"median_ms": float(np.median(a)), "p10_ms": float(np.percentile(a, 10)),
+            "p90_ms": float(np.percentile(a, 90)), "samples": int(a.size)}
+
+
 # ------------------------------------------------------------------ inputs
 class GpuInputs:
     """One workload's inputs on the GPU, prepared with the library's own
     quantisers from the seeded bf16 draws, in `copies` resident copies.
     W4A16: NVFP4 weights, bf16 x.  W4A4: NVFP4 weights and x (x's global
-    scale folded into w1_alpha); fc2_input_scale is 1 (not calibrated: these
-    inputs are for timing).  MXFP8_MXFP4: MXFP4 weights, MXFP8 x."""
+    scale folded into w1_alpha) and fc2_input_scale calibrated on the device
+    (moe_fc2_input_scale over the batch's routes, folded into w2_alpha).
+    MXFP8_MXFP4: MXFP4 weights, MXFP8 x."""
 
     def __init__(self, wl, copies: int):
         import torch
@@ -62,6 +76,7 @@ class GpuInputs:
         u8 = dict(dtype=torch.uint8, device=dev)
         self.x_sf = None
         self.fc2 = None
+        self.ids = torch.from_numpy(self.topk_ids_np).to(dev)
         if wl.mode == moe.MXFP8_MXFP4:
             self.w1 = torch.empty((E, R1, H // 2), **u8)
             self.w1_sf = torch.empty((E, R1, H // 32), **u8)
@@ -92,12 +107,21 @@ class GpuInputs:
                 self.x_sf = torch.empty((M, H // 16), **u8)
                 moe.moe_quantize_nvfp4(xb, 1, M, H, xg, self.x, self.x_sf)
                 self.w1_alpha *= xg
-                self.fc2 = torch.ones(1, dtype=torch.float32, device=dev)
+                # calibration pass on the device: max |y1| / (6 * 448) over the batch's routes
+                tile = moe.default_tile(M, wl.top_k, wl.num_experts, E, wl.mode)
+                plan = moe.moe_sort(self.ids, wl.num_experts, E, wl.local_expert_offset, tile)
+                self.fc2 = torch.empty(1, dtype=torch.float32, device=dev)
+                moe.moe_fc2_input_scale(self.x, self.x_sf, plan, self.w1, self.w1_sf, self.w1_alpha, H, I, self.fc2,
+                                        activation=wl.activation, swiglu_alpha=wl.swiglu_alpha,
+                                        swiglu_beta=wl.swiglu_beta, swiglu_limit=wl.swiglu_limit,
+                                        situ_beta=wl.situ_beta, situ_linear_beta=wl.situ_linear_beta)
+                self.w2_alpha *= self.fc2
+                torch.cuda.synchronize()
+                self.fc2_value = float(self.fc2.cpu()[0])
             else:
                 self.x = xb
         torch.cuda.synchronize()
         del w1b, w2b
-        self.ids = torch.from_numpy(self.topk_ids_np).to(dev)
         _, wts = synth.make_routing(wl)
         self.w = torch.from_numpy(wts).to(dev)
         # resident copies, rotated step by step
@@ -136,25 +160,34 @@ def _scale_kw(g, scaled: bool):
                 fc2_bias=torch.full((E, H), 0.01, dtype=torch.float32, device="cuda"))
 
 
-def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False):
+def _forwarder(moe, g, wl, out, opts):
+    E, H, I = wl.num_local_experts, wl.H, wl.I
+
+    def step(i):
+        x, ids, w, w1, w1s, w1a, w2, w2s, w2a, xs = g.copies[i % len(g.copies)]
+        moe.moe_forward(x, xs, ids, w, w1, w1s, w1a, w2, w2s, w2a, wl.num_experts, wl.top_k, E,
+                        wl.local_expert_offset, wl.mode, out, H, I, opts=opts)
+    return step
+
+
+def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False, latency: int = 0):
     """Times `steps` forwards replayed from a HIP graph that holds `copies`
     forwards, one per resident input copy (no host work between launches).
-    HIP events on the replay stream bracket the timed replays."""
+    HIP events on the replay stream bracket the timed replays.  With
+    latency > 0, also per-forward times: one graph per copy, `latency`
+    replays rotating over the copies (cold) and on one copy (warm), an event
+    between consecutive replays."""
     import torch
 
     import mixture_experts_forward_moe_amd as moe
     g = GpuInputs(wl, copies)
     H, I, E = wl.H, wl.I, wl.num_local_experts
     tile = moe.default_tile(wl.M, wl.top_k, wl.num_experts, E, wl.mode)
-    ws = torch.zeros(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.M, H), dtype=torch.int16, device="cuda")
     skw = _scale_kw(g, scaled)
     opts = _opts(moe, wl, ws, tile, fc2=g.fc2, **skw)
-
-    def step(i):
-        x, ids, w, w1, w1s, w1a, w2, w2s, w2a, xs = g.copies[i % len(g.copies)]
-        moe.moe_forward(x, xs, ids, w, w1, w1s, w1a, w2, w2s, w2a, wl.num_experts, wl.top_k, E,
-                        wl.local_expert_offset, wl.mode, out, H, I, opts=opts)
+    step = _forwarder(moe, g, wl, out, opts)
 
     for i in range(max(warmup, copies)):  # eager warm-up (also caches the launch shape)
         step(i)
@@ -177,24 +210,45 @@ def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False):
     dt = time.perf_counter() - t0
     n = reps * copies
     gpu_ms = e0.elapsed_time(e1)
-    routes, active = g.local_stats()
-    del graph, g
+    res = dict(steps=n, seconds=dt, ms_per_step=dt * 1e3 / n, gpu_ms_per_step=gpu_ms / n, tile=tile)
+    del graph
+    if latency:
+        singles = []
+        for i in range(copies):
+            gi = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gi):
+                step(i)
+            singles.append(gi)
+        for which, order in (("cold", [i % copies for i in range(latency)]), ("warm", [0] * latency)):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(latency + 1)]
+            for i in range(copies):
+                singles[i].replay()
+            torch.cuda.synchronize()
+            ev[0].record()
+            for i, c in enumerate(order):
+                singles[c].replay()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            res[which] = pct([ev[i].elapsed_time(ev[i + 1]) for i in range(latency)])
+        del singles
+    res["local_routes"], res["active_experts"] = g.local_stats()
+    del g
     torch.cuda.empty_cache()
-    return dict(steps=n, seconds=dt, ms_per_step=dt * 1e3 / n, gpu_ms_per_step=gpu_ms / n, tile=tile,
-                local_routes=routes, active_experts=active)
+    return res
 
 
-def time_phases(wl, steps: int, warmup: int, copies: int, scaled: bool = False):
+def time_phases(wl, steps: int, warmup: int, copies: int, scaled: bool = False, plan_out: dict | None = None):
     """Times `steps` eager forwards, then the same steps again with HIP
     events that moe_forward records between its launches on the same
-    stream (per-kernel durations)."""
+    stream (per-kernel durations, and per-step forward times for the
+    percentiles)."""
     import torch
 
     import mixture_experts_forward_moe_amd as moe
     g = GpuInputs(wl, copies)
     H, I, E = wl.H, wl.I, wl.num_local_experts
     tile = moe.default_tile(wl.M, wl.top_k, wl.num_experts, E, wl.mode)
-    ws = torch.zeros(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.M, H), dtype=torch.int16, device="cuda")
     nev = moe.NUM_PHASE_EVENTS
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
@@ -205,31 +259,35 @@ def time_phases(wl, steps: int, warmup: int, copies: int, scaled: bool = False):
     skw = _scale_kw(g, scaled)
     opts = _opts(moe, wl, ws, tile, fc2=g.fc2, **skw)
     opts_ev = [_opts(moe, wl, ws, tile, fc2=g.fc2, phase_events=events[i], **skw) for i in range(steps)]
-
-    def step(i, o):
-        x, ids, w, w1, w1s, w1a, w2, w2s, w2a, xs = g.copies[i % len(g.copies)]
-        moe.moe_forward(x, xs, ids, w, w1, w1s, w1a, w2, w2s, w2a, wl.num_experts, wl.top_k, E,
-                        wl.local_expert_offset, wl.mode, out, H, I, opts=o)
+    step = _forwarder(moe, g, wl, out, opts)
 
     for i in range(warmup):
-        step(i, opts)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, opts)
+        step(i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     for i in range(steps):
-        step(i, opts_ev[i])
+        _forwarder(moe, g, wl, out, opts_ev[i])(i)
     torch.cuda.synchronize()
     names = ["sort", "gemm1", "gemm2", "finalize"]
     per = {n: float(np.mean([events[i][k].elapsed_time(events[i][k + 1]) for i in range(steps)]))
            for k, n in enumerate(names)}
+    fwd = pct([events[i][0].elapsed_time(events[i][nev - 1]) for i in range(steps)])
     routes, active = g.local_stats()
+    if plan_out is not None:
+        # the plan this forward used, read back from its workspace
+        p = moe.MoePlan(wl.M, wl.top_k, E, tile, forward_workspace=ws)
+        plan_out.update(tile=tile, p2e=p.permuted_to_expanded.cpu().numpy(),
+                        tile_expert=p.tile_to_expert.cpu().numpy(), tile_limit=p.tile_to_mn_limit.cpu().numpy(),
+                        num_tiles=int(p.num_tiles.cpu()[0]))
+    res = dict(steps=steps, seconds=dt, ms_per_step=dt * 1e3 / steps, tile=tile, phase_ms=per, forward=fwd,
+               local_routes=routes, active_experts=active, fc2_input_scale=getattr(g, "fc2_value", None))
     del g
     torch.cuda.empty_cache()
-    return dict(steps=steps, seconds=dt, ms_per_step=dt * 1e3 / steps, tile=tile, phase_ms=per,
-                local_routes=routes, active_experts=active)
+    return res
 
 
 # ------------------------------------------------------------------ algorithmic work
@@ -283,27 +341,127 @@ def counter_traffic(kernel: str, workload: str):
     return rec["traffic_bytes_per_launch"]
 
 
+# ------------------------------------------------------------------ routing locality
+def locality_report(plan: dict, wl, tiles=(128, 256), seed: int = 4):
+    """Distinct 2 MiB pages of x a GEMM1 tile gathers from (MXFP8 x rows of
+    H bytes), computed on the host from the plan the forward used: for its
+    stable route order, and for a simulated grid-stride arrival order (each
+    of G = 256 workgroups x 1024 threads takes routes t, t + G, ...; inside
+    one stride the arrival order is a seeded random permutation) at the same
+    per-expert tile padding.  Tiles of 128 slots (this build's) and of 256
+    (the pages' large-batch tile) are both counted."""
+    k, H = wl.top_k, wl.H
+    page = 2 << 20
+    p2e = plan["p2e"]
+    nt, T0 = plan["num_tiles"], plan["tile"]
+    by_expert = {}
+    for i in range(nt):  # each expert's rows in the plan's (stable) order
+        by_expert.setdefault(int(plan["tile_expert"][i]), []).append(p2e[i * T0:plan["tile_limit"][i]])
+    experts = [np.concatenate(v).astype(np.int64) for v in by_expert.values()]
+    assert sum(e.size for e in experts) == int((p2e >= 0).sum())
+    G = 256 * 1024
+    rng = np.random.default_rng(seed)
+    R = wl.M * k
+    rank = np.empty(R, np.int64)   # simulated arrival position of each route
+    for s in range(0, R, G):
+        rank[s:min(R, s + G)] = s + rng.permutation(min(R, s + G) - s)
+
+    def pages_per_tile(order_rows, T):
+        out = []
+        for rows in order_rows:
+            for i in range(0, rows.size, T):
+                toks = rows[i:i + T] // k
+                lo = (toks * H) // page
+                hi = (toks * H + H - 1) // page
+                out.append(np.unique(np.concatenate([lo, hi])).size)
+        a = np.asarray(out)
+        return {"mean": float(a.mean()), "median": float(np.median(a)), "max": int(a.max()), "tiles": int(a.size)}
+
+    rep = {"unit": "distinct 2 MiB pages of x per GEMM1 tile", "x_row_bytes": H,
+           "grid_stride_simulation": "G = 256 x 1024 threads, seeded random order within each stride"}
+    for T in tiles:
+        stable = pages_per_tile(experts, T)
+        strided = pages_per_tile([e[np.argsort(rank[e], kind="stable")] for e in experts], T)
+        rep[f"tile{T}"] = {"stable_order": stable, "grid_stride_order": strided}
+    return rep
+
+
 # ------------------------------------------------------------------ cpu baseline
-def cpu_baseline(wl, min_seconds=10.0):
-    """The oracle as it stands, on the host cores, over every token of the
-    workload (repeated until ~min_seconds of CPU work)."""
+def cpu_baseline(headline: str, min_seconds: float = 2.0):
+    """The oracle as it stands, on the host cores: each workload's forward
+    after its inputs are quantised (input preparation is not timed).  The
+    decode and tiny workloads run all their tokens repeatedly for about
+    min_seconds; prefill and W4A4 one plan-based pass over every token; the
+    M = 65536 MX workload its routing plan for all tokens plus the per-token
+    forward of its 1024 sampled tokens (a sampled rate)."""
     import oracle
     import synth
-    p = oracle.quantize_problem(synth.make_raw(wl))
-    toks = np.arange(wl.M, dtype=np.int32)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.forward_tokens(p, toks)
-        n += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
-    return dict(value=wl.M * n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"all {wl.M} tokens of {wl.name}, {n} pass(es) in {dt:.1f} s (fp64 C oracle, OpenMP)")
+    per = {}
+    for name, wl in synth.WORKLOADS.items():
+        t_prep = time.perf_counter()
+        p = oracle.quantize_problem(synth.make_raw(wl))
+        prep = time.perf_counter() - t_prep
+        ids = p.topk_ids
+        local = (ids >= wl.local_expert_offset) & (ids < wl.local_expert_offset + wl.num_local_experts)
+        if wl.sample_tokens:
+            toks = synth.sample_tokens(wl.seed, wl.M, wl.sample_tokens)
+            t0 = time.perf_counter()
+            oracle.sort(ids, wl.num_local_experts, wl.local_expert_offset, 128)
+            t_plan = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            oracle.forward_tokens(p, toks)
+            dt = time.perf_counter() - t0
+            routes = int(local[toks].sum())
+            per[name] = {"tokens_per_s": toks.size / dt, "gflops": flops(wl, routes) / dt / 1e9, "seconds": dt,
+                         "plan_seconds": t_plan, "sample": f"plan of all {wl.M} tokens; forward of {toks.size} "
+                         f"sampled tokens (sampled rate)", "prep_seconds": prep}
+        elif wl.M <= 64:
+            toks = np.arange(wl.M, dtype=np.int32)
+            n, t0 = 0, time.perf_counter()
+            while True:
+                oracle.forward_tokens(p, toks)
+                n += 1
+                if time.perf_counter() - t0 >= min_seconds:
+                    break
+            dt = time.perf_counter() - t0
+            per[name] = {"tokens_per_s": wl.M * n / dt, "gflops": n * flops(wl, int(local.sum())) / dt / 1e9,
+                         "seconds": dt, "sample": f"all {wl.M} tokens, {n} pass(es)", "prep_seconds": prep}
+        else:
+            t0 = time.perf_counter()
+            oracle.forward_plan(p, 64)
+            dt = time.perf_counter() - t0
+            per[name] = {"tokens_per_s": wl.M / dt, "gflops": flops(wl, int(local.sum())) / dt / 1e9,
+                         "seconds": dt, "sample": f"all {wl.M} tokens, one plan-based pass", "prep_seconds": prep}
+        log(f"bench: cpu oracle {name}: {per[name]['tokens_per_s']:.1f} tokens/s")
+    h = per[headline]
+    return dict(value=h["tokens_per_s"], unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{headline}: {h['sample']} ({h['seconds']:.1f} s, fp64 C oracle, OpenMP); every "
+                       f"workload in per_config", gflops=h["gflops"], per_config=per)
 
 
-# ------------------------------------------------------------------ counter calibration
+# ------------------------------------------------------------------ copy bandwidth
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 20):
+    """A plain device-to-device copy of nbytes: bytes read plus written per
+    second (the streaming bandwidth this machine reaches; the second roofline
+    denominator)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_copied": nbytes, "ms_per_copy": ms, "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
 def copy_calibration(steps: int, nbytes: int = 1 << 28):
     """A plain device-to-device copy of nbytes, `steps` times: its
     FETCH_SIZE / WRITE_SIZE per dispatch against nbytes gives the factor
@@ -326,14 +484,37 @@ def copy_calibration(steps: int, nbytes: int = 1 << 28):
 
 
 # ------------------------------------------------------------------ main
+def secondary(name, wl, r, peak, copy_gbs, note):
+    fl = flops(wl, r["local_routes"])
+    ms = r["forward"]["median_ms"]
+    tf = fl / (ms * 1e-3) / 1e12
+    wb = weight_bytes(wl, r["active_experts"])
+    d = {"workload": wl.name, "M": wl.M, "H": wl.H, "I": wl.I, "local_experts": wl.num_local_experts,
+         "tokens_per_s": wl.M * r["steps"] / r["seconds"], "ms_per_step": r["ms_per_step"], "forward": r["forward"],
+         "tile": r["tile"], "local_routes": r["local_routes"], "tflops": tf, "mfma_frac": tf / peak,
+         "peak_tflops": peak, "phase_ms": r["phase_ms"], "weight_bytes": wb,
+         "weights_GBps": wb / (ms * 1e-3) / 1e9, "weights_hbm_frac": wb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+         "weights_copy_frac": wb / (ms * 1e-3) / 1e9 / copy_gbs,
+         "note": note + "; rates from the median per-step forward time (HIP events)"}
+    g1f = (2.0 if wl.activation == 2 else 4.0) * wl.H * wl.I * r["local_routes"] / (
+        r["phase_ms"]["gemm1"] * 1e-3) / 1e12
+    d["gemm1_tflops"] = g1f
+    d["gemm1_mfma_frac"] = g1f / peak
+    if r.get("fc2_input_scale") is not None:
+        d["fc2_input_scale"] = r["fc2_input_scale"]
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=6, help="resident input copies rotated over steps")
+    ap.add_argument("--latency-samples", type=int, default=300, help="forwards timed one by one for percentiles")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--workload", default="w4a16_decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (scales the HBM byte counters)")
@@ -354,8 +535,12 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     wl = synth.WORKLOADS[args.workload]
 
-    log(f"bench: {wl.name}: {args.steps} steps after {args.warmup} warm-up (graph replay)")
-    r = time_graph(wl, args.steps, args.warmup, args.copies)
+    log("bench: streaming copy bandwidth")
+    cbw = copy_bandwidth()
+    copy_gbs = cbw["GBps"]
+    log(f"bench: {wl.name}: {args.steps} steps after {args.warmup} warm-up (graph replay), then "
+        f"{args.latency_samples} forwards one by one")
+    r = time_graph(wl, args.steps, args.warmup, args.copies, latency=args.latency_samples)
     routes, active = r["local_routes"], r["active_experts"]
     by = w4a16_bytes(wl, routes, active)
     fl = flops(wl, routes)
@@ -393,7 +578,14 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "dec_gemm1_kernel + dec_gemm2_kernel (one decode forward)",
                      "achieved": f_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": f_gbs / HBM_PEAK_GBS,
                      "traffic": counter_traffic("dec_forward", wl.name),
-                     "algorithmic_bytes": by["forward"], "avg_ms": f_ms},
+                     "algorithmic_bytes": by["forward"], "avg_ms": f_ms,
+                     "copy_GBps": copy_gbs, "frac_of_copy": f_gbs / copy_gbs},
+        "latency": {"cold": r["cold"], "warm": r["warm"],
+                    "cold_hbm_frac": by["forward"] / (r["cold"]["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "warm_hbm_frac": by["forward"] / (r["warm"]["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "note": "per-forward times, one graph replay each: cold rotates the resident copies (no "
+                            "MALL reuse), warm replays one copy (weights found in the 256 MB MALL)"},
+        "copy_bandwidth": cbw,
         "kernels": {"dec_gemm1_kernel": {"avg_ms": k1_ms, "algorithmic_bytes": by["gemm1"],
                                          "GBps": by["gemm1"] / (k1_ms * 1e-3) / 1e9},
                     "dec_gemm2_kernel": {"avg_ms": k2_ms, "algorithmic_bytes": by["gemm2"],
@@ -401,43 +593,32 @@ def main():
                                          "note": "includes the route-order finalize of its last workgroups"},
                     "timing": "eager steps, HIP events between the launches"},
         "weights": {"bytes": by["weights"], "GBps": w_gbs, "hbm_frac": w_gbs / HBM_PEAK_GBS,
-                    "tflops": fl / (f_ms * 1e-3) / 1e12},
+                    "copy_frac": w_gbs / copy_gbs, "tflops": fl / (f_ms * 1e-3) / 1e12},
     }
     if not args.no_secondary:
         wl2 = synth.WORKLOADS["w4a16_prefill"]
-        steps2 = max(10, args.steps // 10)
+        steps2 = max(20, args.steps // 10)
         log(f"bench: {wl2.name}: {steps2} steps (eager, per-kernel events)")
         r2 = time_phases(wl2, steps2, max(3, args.warmup // 4), args.copies)
-        fl2 = flops(wl2, r2["local_routes"])
-        tf2 = fl2 / (r2["ms_per_step"] * 1e-3) / 1e12
-        g1f = 4.0 * wl2.H * wl2.I * r2["local_routes"] / (r2["phase_ms"]["gemm1"] * 1e-3) / 1e12
-        line["prefill"] = {"workload": wl2.name, "M": wl2.M, "tokens_per_s": wl2.M * steps2 / r2["seconds"],
-                           "ms_per_step": r2["ms_per_step"], "tile": r2["tile"], "local_routes": r2["local_routes"],
-                           "tflops": tf2, "mfma_frac": tf2 / BF16_PEAK_TFLOPS, "gemm1_tflops": g1f,
-                           "gemm1_mfma_frac": g1f / BF16_PEAK_TFLOPS, "phase_ms": r2["phase_ms"],
-                           "peak_tflops": BF16_PEAK_TFLOPS}
-    if not args.no_secondary:
-        # the other two quantisation modes, on their parity configurations
-        for name, key, peak, steps3, note in (
-                ("w4a4", "w4a4_nvfp4", BF16_PEAK_TFLOPS, 10, "NVFP4 x and weights, bf16 MFMA after decode"),
-                ("mx", "mxfp8_mxfp4_large", FP8_PEAK_TFLOPS, 4,
+        line["prefill"] = secondary("prefill", wl2, r2, BF16_PEAK_TFLOPS, copy_gbs, "W4A16, bf16 MFMA")
+        for name, key, peak, steps3, copies3, note in (
+                ("w4a4", "w4a4_nvfp4", BF16_PEAK_TFLOPS, 20, args.copies,
+                 "NVFP4 x and weights, bf16 MFMA after decode; fc2_input_scale calibrated on the device"),
+                ("mx", "mxfp8_mxfp4_large", FP8_PEAK_TFLOPS, 6, 1,
                  "MXFP8 x, MXFP4 weights, scaled fp8 x fp4 MFMA (peak: dense fp8)")):
             wl3 = synth.WORKLOADS[key]
             log(f"bench: {wl3.name}: {steps3} steps (eager, per-kernel events)")
-            r3 = time_phases(wl3, steps3, 2, 1)
-            fl3 = flops(wl3, r3["local_routes"])
-            tf3 = fl3 / (r3["ms_per_step"] * 1e-3) / 1e12
-            wb = weight_bytes(wl3, r3["active_experts"])
-            line[name] = {"workload": wl3.name, "M": wl3.M, "H": wl3.H, "I": wl3.I,
-                          "local_experts": wl3.num_local_experts, "tokens_per_s": wl3.M * steps3 / r3["seconds"],
-                          "ms_per_step": r3["ms_per_step"], "tile": r3["tile"], "local_routes": r3["local_routes"],
-                          "tflops": tf3, "mfma_frac": tf3 / peak, "peak_tflops": peak, "phase_ms": r3["phase_ms"],
-                          "weight_bytes": wb, "weights_hbm_frac": wb / (r3["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                          "note": note}
-    if not args.no_secondary:
-        # the other GEMM epilogues on the decode and prefill workloads (GeGLU-tanh, SiTU, and SwiGLU with
-        # the up half's own scale, FC1 / FC2 biases and routed_scaling_factor 1.75): the decode forward in graph replay
-        # (same roofline unit as the headline) and the prefill GEMM1 with per-kernel events
+            plan = {} if name == "mx" else None
+            r3 = time_phases(wl3, steps3, 2, copies3, plan_out=plan)
+            line[name] = secondary(name, wl3, r3, peak, copy_gbs, note)
+            if plan:
+                log("bench: routing locality of the large-batch plan")
+                line[name]["locality"] = locality_report(plan, wl3)
+    if not args.no_secondary and not args.no_variants:
+        # the other GEMM epilogues on the decode and prefill workloads (GeGLU-tanh, SiTU, ReLU^2, and SwiGLU
+        # with the up half's own scale, FC1 / FC2 biases and routed_scaling_factor 1.75): the decode
+        # forward in graph replay (same roofline unit as the headline) and the prefill GEMM1 with per-kernel
+        # events
         import dataclasses
         acts = {}
         for name, kw in (("geglu_tanh", dict(activation=1)), ("situ", dict(situ_beta=0.5, situ_linear_beta=1.0)),
@@ -455,8 +636,9 @@ def main():
             if scaled:
                 kw = {"w1_alpha_up": "1.5 x w1_alpha", "fc1_bias": 0.01, "fc2_bias": 0.01,
                       "routed_scaling_factor": 1.75}
-            acts[name] = {"params": kw, "decode_ms_per_forward": rd["gpu_ms_per_step"], "decode_hbm_frac": fd / HBM_PEAK_GBS,
-                          "prefill_gemm1_ms": rp["phase_ms"]["gemm1"], "prefill_gemm1_mfma_frac": g1 / BF16_PEAK_TFLOPS}
+            acts[name] = {"params": kw, "decode_ms_per_forward": rd["gpu_ms_per_step"],
+                          "decode_hbm_frac": fd / HBM_PEAK_GBS, "prefill_gemm1_ms": rp["phase_ms"]["gemm1"],
+                          "prefill_gemm1_mfma_frac": g1 / BF16_PEAK_TFLOPS}
         acts["swiglu"] = {"decode_ms_per_forward": f_ms, "decode_hbm_frac": f_gbs / HBM_PEAK_GBS,
                           "prefill_gemm1_ms": line["prefill"]["phase_ms"]["gemm1"],
                           "prefill_gemm1_mfma_frac": line["prefill"]["gemm1_mfma_frac"],
@@ -464,7 +646,7 @@ def main():
         line["epilogue_variants"] = acts
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
-        line["cpu_baseline"] = cpu_baseline(wl)
+        line["cpu_baseline"] = cpu_baseline(wl.name)
     print(json.dumps(line), flush=True)
 
 

@@ -397,6 +397,24 @@ moe_status_t moe_forward_noalloc(const void* x, const uint8_t* x_sf, const int32
 moe_status_t moe_nvfp4_global_scale(const uint16_t* x, int64_t batches, int64_t batch_elems, float* gscale,
                                     moe_stream_t stream);
 
+/* moe_fc2_input_scale: the W4A4 calibration of fc2_input_scale
+ * ("flashinfer.fused_moe.cute_dsl_fused_moe", Parameters fc2_input_scale:
+ * the global scale of GEMM2's NVFP4 input).  Runs GEMM1 of the W4A4 mode on
+ * the plan (the arguments as moe_grouped_gemm1_act, without y1) and writes
+ *   *fc2_input_scale = max |y1| / (6 * 448)   (fp32, correctly rounded)
+ * over every valid route and column, y1 taken after its bf16 rounding and
+ * before any requantisation: the same formula as the NVFP4 global scale of
+ * moe_nvfp4_global_scale.  fc2_input_scale is a device fp32 scalar; it is
+ * also the pass's accumulator, so it must not be read until the pass ends.
+ * Then w2_alpha of the W4A4 forward folds it in (see moe_quant_mode_t).
+ * M = 0 gives 0. */
+moe_status_t moe_fc2_input_scale(const void* x, const uint8_t* x_sf, int64_t x_row_stride, const moe_plan_t* plan,
+                                 const uint8_t* w1, const uint8_t* w1_sf, const float* w1_alpha,
+                                 const float* w1_alpha_up, int H, int I, int activation, float swiglu_alpha,
+                                 float swiglu_beta, float swiglu_limit, float situ_beta, float situ_linear_beta,
+                                 const float* per_token_scale, const float* fc1_bias, float* fc2_input_scale,
+                                 moe_stream_t stream);
+
 /* NVFP4 quantisation of bf16 [batches, rows, cols] (cols % 16 == 0), batch
  * b with global scale gscale[b] (device fp32): block scale
  * E4M3(blockamax / (6 * gscale)), codes E2M1(v / (decode(scale) * gscale)),

@@ -24,7 +24,7 @@ ACT_SWIGLU, ACT_GEGLU_TANH, ACT_RELU2 = 0, 1, 2   # moe_activation_t (SiTU: ACT_
 EXPORTS = [
     "moe_status_string", "moe_route_slots", "moe_plan_workspace_size", "moe_plan_init", "moe_sort",
     "moe_grouped_gemm1_swiglu", "moe_grouped_gemm1_act", "moe_grouped_gemm2", "moe_grouped_gemm2_bias", "moe_finalize", "moe_opts_init", "moe_default_tile",
-    "moe_workspace_size", "moe_forward_plan", "moe_forward", "moe_forward_noalloc", "moe_nvfp4_global_scale", "moe_quantize_nvfp4", "moe_quantize_mx",
+    "moe_workspace_size", "moe_forward_plan", "moe_forward", "moe_forward_noalloc", "moe_fc2_input_scale", "moe_nvfp4_global_scale", "moe_quantize_nvfp4", "moe_quantize_mx",
 ]
 
 
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "moe_forward_plan": ([P, P, SZ, I, I, I, I], I),
             "moe_forward": ([P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I, I, P, P], I),
             "moe_forward_noalloc": ([P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I, I, P, P], I),
+            "moe_fc2_input_scale": ([P, P, I64, P, P, P, P, P, I, I, I, F, F, F, F, F, P, P, P, P], I),
             "moe_nvfp4_global_scale": ([P, I64, I64, P, P], I),
             "moe_quantize_nvfp4": ([P, I64, I64, I64, P, P, P, P], I),
             "moe_quantize_mx": ([P, I64, I64, I, P, P, P], I),
@@ -308,6 +309,16 @@ def moe_forward_noalloc(x, x_sf, topk_ids, topk_weights, w1, w1_sf, w1_alpha, w2
                                      num_local_experts, local_expert_offset, quant_mode, _ptr(out), M, H, I,
                                      ctypes.byref(opts), _stream(stream)), "moe_forward_noalloc")
     return out
+
+
+def moe_fc2_input_scale(x, x_sf, plan: MoePlan, w1, w1_sf, w1_alpha, H, I, fc2_input_scale, activation=ACT_SWIGLU,
+                        swiglu_alpha=1.0, swiglu_beta=0.0, swiglu_limit=FLT_MAX, situ_beta=0.0, situ_linear_beta=0.0,
+                        x_row_stride=0, w1_alpha_up=None, per_token_scale=None, fc1_bias=None, stream=None):
+    """W4A4: fc2_input_scale (device fp32 [1]) = max |y1| / (6 * 448) over the plan's routes."""
+    _check(lib().moe_fc2_input_scale(_ptr(x), _ptr(x_sf), x_row_stride, ctypes.byref(plan.c), _ptr(w1), _ptr(w1_sf),
+                                     _ptr(w1_alpha), _ptr(w1_alpha_up), H, I, activation, swiglu_alpha, swiglu_beta,
+                                     swiglu_limit, situ_beta, situ_linear_beta, _ptr(per_token_scale),
+                                     _ptr(fc1_bias), _ptr(fc2_input_scale), _stream(stream)), "moe_fc2_input_scale")
 
 
 def moe_nvfp4_global_scale(x, batches: int, gscale, stream=None):

@@ -484,6 +484,44 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   return MOE_OK;
 }
 
+moe_status_t moe_fc2_input_scale(const void* x, const uint8_t* x_sf, int64_t x_row_stride, const moe_plan_t* plan,
+                                 const uint8_t* w1, const uint8_t* w1_sf, const float* w1_alpha,
+                                 const float* w1_alpha_up, int H, int I, int activation, float swiglu_alpha,
+                                 float swiglu_beta, float swiglu_limit, float situ_beta, float situ_linear_beta,
+                                 const float* per_token_scale, const float* fc1_bias, float* fc2_input_scale,
+                                 moe_stream_t stream) {
+  if (!plan_ok(plan) || !fc2_input_scale) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t s = shape_check(H, I, MOE_QUANT_W4A4, activation);
+  if (s != MOE_OK) return s;
+  if (!w1 || !w1_sf || !w1_alpha || !x_sf || (plan->M > 0 && !x)) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t row_units = H / 2;
+  if (x_row_stride != 0 && x_row_stride < row_units) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t stride = x_row_stride ? x_row_stride : row_units;
+  if (stride % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  Gemm1Params p = {};
+  s = make_act(activation, swiglu_alpha, swiglu_beta, swiglu_limit, situ_beta, situ_linear_beta, &p.act);
+  if (s != MOE_OK) return s;
+  if (p.act.kind == ACT_RELU2 && w1_alpha_up) return MOE_ERR_INVALID_ARGUMENT;
+  p.mode = MOE_QUANT_W4A4;
+  p.x = x;
+  p.x_sf = x_sf;
+  p.x_row_stride = stride;
+  p.plan = plan;
+  p.w1 = w1;
+  p.w1_sf = w1_sf;
+  p.w1_alpha = w1_alpha;
+  p.w1_alpha_up = w1_alpha_up;
+  p.H = H;
+  p.I = I;
+  p.per_token_scale = per_token_scale;
+  p.fc1_bias = fc1_bias;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned* bits = reinterpret_cast<unsigned*>(fc2_input_scale);
+  if (launch_zero_fill(bits, sizeof(float), st) != hipSuccess) return MOE_ERR_DEVICE;
+  if (plan->M > 0 && launch_gemm1_amax(p, bits, st) != hipSuccess) return MOE_ERR_DEVICE;
+  return dev(launch_gscale_finish(fc2_input_scale, 1, st));
+}
+
 moe_status_t moe_nvfp4_global_scale(const uint16_t* x, int64_t batches, int64_t batch_elems, float* gscale,
                                     moe_stream_t stream) {
   if (batches < 0 || batch_elems < 0 || (batches > 0 && (!x || !gscale))) return MOE_ERR_INVALID_ARGUMENT;

@@ -113,6 +113,11 @@ __global__ void gscale_finish_kernel(float* gs, int64_t batches) {
   if (b < batches) gs[b] = __fdiv_rn(gs[b], 2688.0f);
 }
 
+hipError_t launch_gscale_finish(float* gs, int64_t batches, hipStream_t stream) {
+  gscale_finish_kernel<<<(unsigned)((batches + 255) / 256), 256, 0, stream>>>(gs, batches);
+  return hipGetLastError();
+}
+
 hipError_t launch_nvfp4_global_scale(const uint16_t* x, int64_t batches, int64_t n, float* gs, hipStream_t stream) {
   hipError_t e = launch_zero_fill(gs, sizeof(float) * batches, stream);
   if (e != hipSuccess) return e;

@@ -73,6 +73,7 @@ struct KArgs {
   const float* topk_w;
   float rsf;
   uint16_t* out;        // atomic finalize
+  unsigned* amax;       // GEMM1 calibration: fp32 bits of the largest |y1| (nothing stored); NULL otherwise
 };
 
 template <int MODE>
@@ -373,6 +374,25 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void grouped_gemm_kernel(const KAr
           y[1][m][i] = 0.0f;
         }
       }
+    if (a.amax) {
+      // calibration pass: the largest |y1| over the valid rows and columns
+      // (non-negative floats order like their bit patterns)
+      float mx = 0.0f;
+#pragma unroll
+      for (int m = 0; m < MT; m++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int row = m * 16 + 4 * q + i;
+          if (row < valid && col_ok) {
+            mx = fmaxf(mx, fabsf(y[0][m][i]));
+            if (two) mx = fmaxf(mx, fabsf(y[1][m][i]));
+          }
+        }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      if (lane == 0 && mx > 0.0f) atomicMax(a.amax, __float_as_uint(mx));
+      return;
+    }
     auto store = [&](const float (&ys)[MT][4], const int cx) __attribute__((always_inline)) {
       if constexpr (MODE == M_W4A16) {
         uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
@@ -539,6 +559,33 @@ hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
   a.fc2_scale = p.fc2_input_scale;
   a.Y = p.y1;
   a.Y_sf = p.y1_sf;
+  return dispatch<1, false>(p.mode, bm, a, stream);
+}
+
+hipError_t launch_gemm1_amax(const Gemm1Params& p, unsigned* amax, hipStream_t stream) {
+  KArgs a = {};
+  const int bm = pick_bm(p.plan->tile);
+  plan_args(a, p.plan, bm);
+  a.A = reinterpret_cast<const uint8_t*>(p.x);
+  a.A_sf = p.x_sf;
+  const int64_t stride = p.x_row_stride ? p.x_row_stride : (p.mode == M_W4A4 ? p.H / 2 : p.H);
+  a.a_row_bytes = (p.mode == M_W4A16) ? stride * 2 : stride;
+  a.a_sf_row = (p.mode == M_MX) ? p.H / 32 : p.H / 16;
+  a.W = p.w1;
+  a.W_sf = p.w1_sf;
+  a.alpha = p.w1_alpha;
+  a.alpha_up = p.w1_alpha_up;
+  a.pts = p.per_token_scale;
+  a.bias = p.fc1_bias;
+  a.K = p.H;
+  const int IP = gemm1_pairs(p);
+  a.rows_per_expert = 2 * IP;
+  a.I = IP;
+  a.n_out = p.I;
+  a.n_tiles = (IP + 63) / 64;
+  a.total_tiles = a.m_tiles * a.n_tiles;
+  a.act = p.act;
+  a.amax = amax;
   return dispatch<1, false>(p.mode, bm, a, stream);
 }
 

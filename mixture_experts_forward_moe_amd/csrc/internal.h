@@ -57,6 +57,9 @@ hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream);
 // y1 columns j and I/2 + j
 inline int gemm1_pairs(const Gemm1Params& p) { return p.act.kind == ACT_RELU2 ? p.I / 2 : p.I; }
 hipError_t launch_gemm2(const Gemm2Params& p, hipStream_t stream);
+// GEMM1 without a store: atomically maxes the fp32 bits of |y1| (after its
+// bf16 rounding) over every valid route and column into *amax
+hipError_t launch_gemm1_amax(const Gemm1Params& p, unsigned* amax, hipStream_t stream);
 
 // wide-tile kernels for 128-slot tiles (prefill-sized batches, W4A16 / W4A4)
 bool wide_supported1(const Gemm1Params& p);
@@ -120,6 +123,8 @@ hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 
 // input quantisers
 hipError_t launch_nvfp4_global_scale(const uint16_t* x, int64_t batches, int64_t n, float* gs, hipStream_t stream);
+// gs[b] = (fp32 bits in gs[b]) / (6 * 448), correctly rounded
+hipError_t launch_gscale_finish(float* gs, int64_t batches, hipStream_t stream);
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int64_t batches, int64_t rows, int64_t cols, const float* gs,
                                  uint8_t* q, uint8_t* sf, hipStream_t stream);
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int elem, uint8_t* q, uint8_t* sf,

@@ -36,7 +36,12 @@
  * of two decoded 4/8-bit values is exact in fp64.  Where the pages state an
  * fp32 step (the per-expert scale on the fp32 accumulator, the finalize
  * accumulator) it is taken in fp32.  Quantisation decisions (scale and
- * element codes) are taken in fp32, the precision the GPU kernels decide in.
+ * element codes) are taken in fp32: the pages give every global scale as an
+ * fp32 tensor (w1_alpha, w2_alpha, fc2_input_scale of
+ * "flashinfer.fused_moe.cute_dsl_fused_moe", Parameters), so a block scale
+ * blockamax / (6 * scale) and an element quotient v / (block scale * scale)
+ * are fp32 expressions of fp32 operands, and the OCP conversions (round to
+ * nearest even, saturation) are defined on that fp32 value.
  * Readings of passages the pages leave open are listed where they are used.
  */
 #include <math.h>
