@@ -516,6 +516,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--workload", default="w4a16_decode")
+    ap.add_argument("--only", choices=["prefill", "w4a4", "mx"], default=None,
+                    help="profiling aid: time only this secondary workload (no headline line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -534,6 +536,15 @@ def main():
     moe.lib()  # fail loudly if the native library is missing
     assert torch.cuda.is_available(), "no GPU"
     wl = synth.WORKLOADS[args.workload]
+    if args.only:
+        key = {"prefill": "w4a16_prefill", "w4a4": "w4a4_nvfp4", "mx": "mxfp8_mxfp4_large"}[args.only]
+        wo = synth.WORKLOADS[key]
+        peak = FP8_PEAK_TFLOPS if args.only == "mx" else BF16_PEAK_TFLOPS
+        steps = max(2, args.steps)
+        log(f"bench: {wo.name} only: {steps} steps (eager, per-kernel events)")
+        ro = time_phases(wo, steps, args.warmup, 1 if args.only == "mx" else args.copies)
+        print(json.dumps({args.only: secondary(args.only, wo, ro, peak, float("nan"), "profiling run")}), flush=True)
+        return
 
     log("bench: streaming copy bandwidth")
     cbw = copy_bandwidth()

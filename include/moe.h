@@ -319,7 +319,8 @@ void moe_opts_init(moe_opts_t* opts);
  * picks per batch).  It estimates the routes per local expert as
  * M * top_k / num_experts (the local share of the routes spread over the
  * local experts) and returns 16 up to 16 routes, 32 up to 48, 64 up to 96,
- * else 128. */
+ * else 128 -- or 256 in the MXFP8_MXFP4 mode above 384 routes, the tile of
+ * the large-batch benchmark in FlashInfer pull request 4440. */
 int moe_default_tile(int M, int top_k, int num_experts, int num_local_experts, moe_quant_mode_t mode);
 
 /* Bytes of device workspace moe_forward needs: the caller-owned buffers of

@@ -299,7 +299,6 @@ void moe_opts_init(moe_opts_t* o) {
 }
 
 int moe_default_tile(int M, int top_k, int num_experts, int num_local_experts, moe_quant_mode_t mode) {
-  (void)mode;
   // routes per local expert, expected: of the M * top_k routes, those that
   // land on this GPU's num_local_experts of num_experts
   const int El = num_local_experts > 0 ? num_local_experts : 1;
@@ -308,6 +307,9 @@ int moe_default_tile(int M, int top_k, int num_experts, int num_local_experts, m
   if (per_expert <= 16) return 16;
   if (per_expert <= 48) return 32;
   if (per_expert <= 96) return 64;
+  // the MX mode's large-batch kernel works on 256-slot tiles (the tile of
+  // the large-batch benchmark of pull request 4440)
+  if (mode == MOE_QUANT_MXFP8_MXFP4 && per_expert > 384) return 256;
   return 128;
 }
 

@@ -73,6 +73,12 @@ bool mx_supported2(const Gemm2Params& p);
 hipError_t launch_gemm1_mx(const Gemm1Params& p, hipStream_t stream);
 hipError_t launch_gemm2_mx(const Gemm2Params& p, hipStream_t stream);
 
+// MXFP8 x MXFP4 on 256-slot tiles (large batches): LDS-DMA staged, 256 x 256 per workgroup
+bool mxw_supported1(const Gemm1Params& p);
+bool mxw_supported2(const Gemm2Params& p);
+hipError_t launch_gemm1_mxw(const Gemm1Params& p, hipStream_t stream);
+hipError_t launch_gemm2_mxw(const Gemm2Params& p, hipStream_t stream);
+
 // weight-streaming kernels for 16-slot tiles (decode-sized batches)
 bool stream_supported(int mode, const moe_plan_t* plan, int H, int I);
 hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream);

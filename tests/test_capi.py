@@ -194,7 +194,9 @@ def test_default_tile_counts_local_routes():
     assert moe.default_tile(16, 2, 8, 8, 0) == 16            # tiny: 4
     assert moe.default_tile(512, 8, 128, 128, 1) == 32       # W4A4: 32
     assert moe.default_tile(4096, 8, 256, 32, 0) == 128      # prefill: 128
-    assert moe.default_tile(65536, 8, 256, 32, 2) == 128     # MX large batch: 2048
+    assert moe.default_tile(65536, 8, 256, 32, 2) == 256     # MX large batch: 2048, the 256-slot kernel
+    assert moe.default_tile(65536, 8, 256, 32, 0) == 128     # the same batch in W4A16
+    assert moe.default_tile(12288, 8, 256, 32, 2) == 128     # MX at 384 routes per expert
     # the same batch over 8x the global experts puts 1/8 of the routes here
     assert moe.default_tile(1024, 8, 64, 8, 0) == 128        # 128 per expert
     assert moe.default_tile(1024, 8, 512, 8, 0) == 16        # 16 per expert

@@ -82,7 +82,7 @@ def y1_values(mode, q, sf):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("tile", [16, 64, 128])
+@pytest.mark.parametrize("tile", [16, 64, 128, 256])
 def test_gemm1_and_gemm2_stages(name, tile):
     import torch
 
@@ -126,7 +126,7 @@ def test_gemm1_and_gemm2_stages(name, tile):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("tile", [0, 16, 32, 128])
+@pytest.mark.parametrize("tile", [0, 16, 32, 128, 256])
 def test_forward(name, tile):
     import torch
 
