@@ -1,45 +1,53 @@
-// gemm_mxw.hip -- grouped GEMM1 (+ SwiGLU + MXFP8 requantisation) and GEMM2
-// for MXFP8 activations x MXFP4 weights on 256-slot route tiles (the
-// large-batch tile of pull request 4440's benchmark).
+// gemm_mxw.hip -- grouped GEMM1 (+ gated activation + MXFP8 requantisation)
+// and GEMM2 for MXFP8 activations x MXFP4 weights on 256-slot route tiles
+// (the large-batch tile of pull request 4440's benchmark).
 //
 // The computation is the one gemm_mx.hip states (pull request 4440,
 // description: MXFP8 activations and FC1 intermediate, MXFP4 weights, E8M0
 // block-32 scales; "vllm.models.flint.ops.moe_cute", grouped_moe, for the
 // plan):
-//   GEMM1: y1 = SwiGLU(alpha1[e] * x W1[e]^T), gate/up in fp32, rounded once
-//          to bf16, then requantised to MXFP8 from that bf16 value.
+//   GEMM1: y1 = act(alpha1[e] * x W1[e]^T), gate/up in fp32, rounded once to
+//          bf16, then requantised to MXFP8 from that bf16 value.
 //   GEMM2: y2 = alpha2[e] * y1 W2[e]^T, bf16 rows or weighted packed-bf16
 //          atomics into out.
 //
-// Shape for gfx950 (v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 A x E2M1 B):
-//  - a workgroup of 4 wavefronts owns one 256-slot tile and 256 weight rows;
-//    wavefront (wm, wn) = (wave >> 1, wave & 1) computes slots 128 wm .. and
-//    weight rows 128 wn .. as 8 x 8 tiles of 16 x 16 (256 accumulators).
-//    GEMM1: the wavefront's 128 weight rows are 64 gate rows and the 64
-//    matching up rows, so SwiGLU pairs and whole 32-column MXFP8 blocks of y1
-//    stay inside one lane group.
+// Shape for gfx950 (v_mfma_scale_f32_32x32x64_f8f6f4, E2M1 weights as the A
+// operand, E4M3 activations as B):
+//  - a work item is (plan tile of 256 slots, block of 256 weight rows); a
+//    workgroup of 4 wavefronts computes it, wavefront (ww, ws) = (wave & 1,
+//    wave >> 1) the 128 weight rows 128 ww .. and the 128 slots 128 ws .. as
+//    4 x 4 MFMA tiles of 32 x 32 (256 accumulators).  GEMM1: a wavefront's
+//    128 weight rows are 64 gate rows (tiles 0, 1) and the 64 matching up
+//    rows (tiles 2, 3), so SwiGLU pairs sit in one lane.
+//  - the weight rows of an MFMA tile are loaded in the order that gives lane
+//    (slot r, half h) the 16 consecutive output columns 16 h .. 16 h + 15 of
+//    the tile: a 32-column MXFP8 block of one y1 row is two lanes, its codes
+//    one 16-byte store per lane.
 //  - every operand goes global -> LDS with the LDS-DMA loads
-//    (global_load_lds, 16 bytes a lane; 4 bytes for the scale words), into a
-//    ring of 3 stages of 128 K (activations 32 KiB, weights 16 KiB, their
-//    E8M0 scales 1 KiB each): stage s + 2 is in flight while stage s feeds
-//    the MFMAs, and no register holds data in transit.  The waits are
-//    explicit: a wave waits for its own loads of stage s (vmcnt counts the
-//    later stage's loads, which complete after them), then the workgroup
-//    barrier (s_barrier alone: a release fence would wait for every load in
-//    flight) makes everyone's loads of stage s visible.
+//    (global_load_lds: 16 bytes a lane, 4 for scale words and route ids)
+//    into a ring of 3 stages of 128 K; the ring runs on across work items,
+//    so the next item's first stages load while this item finishes and
+//    writes its epilogue.  A wavefront issues the same number of such loads
+//    every stage (activations 8, their scales 1, weights 4, their scales 1,
+//    the next item's route ids 1, and its bias and this item's routing
+//    weights when the epilogue uses them), so "stage s + 1 has landed" is a
+//    fixed vmcnt wait, then a bare s_barrier (a release fence would also
+//    wait for the loads in flight) publishes every wavefront's part.  The
+//    epilogue reads only LDS and scalars: a vector load there would make
+//    the compiler wait for every DMA in flight.
+//  - operand fragments are double-buffered in registers per 64-K half
+//    stage: the half-stage reads go out while the other half's 16 MFMAs
+//    run, so the matrix cores do not wait for LDS.  One barrier per stage.
 //  - the LDS positions a DMA load fills are fixed (lane i writes 16 i past
-//    the wave's base), so the swizzles that keep the MFMA operand reads free
-//    of bank conflicts are applied on the source side: each lane loads the
-//    16-byte chunk that belongs at its position.  The scale words are placed
-//    so that one lane's eight row tiles have their scales in 32 consecutive
-//    bytes (two 16-byte reads per stage).
-//  - per 128-K stage a wavefront issues 64 MFMAs (2048 cycles at the fp8
-//    rate) against 28 LDS reads of 16 bytes and 14 LDS-DMA loads.
-//  - every row tile runs its MFMAs, also past the tile's routes (a branch
-//    around them would serialise the operand reads with the MFMAs); only the
-//    epilogue skips row tiles without routes.  Work items (tile, weight-row
-//    block) go heaviest tile first, a pair of tiles and all its weight-row
-//    blocks per XCD at a time (see the kernel).
+//    the wave's base), so the swizzles that keep fragment reads free of bank
+//    conflicts (64 banks of 4 bytes, 8 lanes a clock for 16-byte reads) are
+//    applied on the source side: each lane loads the chunk that belongs at
+//    its position.
+//  - every MFMA tile runs, also past a tile's routes; only the epilogue
+//    skips slots without routes.  Items go in plan order, groups of GT
+//    consecutive tiles (tiles of one expert, mostly) per XCD with all their
+//    weight-row blocks, so an XCD's workgroups share each weight block among
+//    GT tiles in that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -47,25 +55,37 @@
 
 #include "device_common.h"
 #include "internal.h"
-#include "tile_order.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int MT = 256;                     // threads
-constexpr int MS = 256;                     // slots per tile
-constexpr int MN = 256;                     // weight rows per workgroup
-constexpr int MK = 128;                     // K per stage
-constexpr int NBUF = 3;                     // stages in the LDS ring
-constexpr int A_OFF = 0;                    // activations [256 slots][8 chunks of 16 B], swizzled
-constexpr int AS_OFF = MS * MK;             // activation scale words [wm][r16][m] x 4 B
-constexpr int B_OFF = AS_OFF + MS * 4;      // weights [256 rows][4 chunks of 16 B], swizzled
-constexpr int BS_OFF = B_OFF + MN * MK / 2; // weight scale words [wn][r16][n] x 4 B
-constexpr int STAGE = BS_OFF + MN * 4;      // 51200 B
-constexpr int LDS_BYTES = NBUF * STAGE;     // 150 KiB
-constexpr int DMA_PER_STAGE = 8 + 1 + 4 + 1;  // LDS-DMA loads a wavefront issues per stage
-constexpr int GT = 4;                       // tiles sharing the weight blocks on one XCD
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int MT = 256;                          // threads
+constexpr int MS = 256;                          // slots per tile
+constexpr int MN = 256;                          // weight rows per item
+constexpr int MK = 128;                          // K per stage
+constexpr int NBUF = 3;                          // stages in the LDS ring
+constexpr int X_OFF = 0;                         // activations [256 slots][8 chunks of 16 B]
+constexpr int XS_OFF = MS * MK;                  // activation scale words
+constexpr int W_OFF = XS_OFF + MS * 4;           // weights [256 rows][4 chunks of 16 B]
+constexpr int WS_OFF = W_OFF + MN * MK / 2;      // weight scale words
+constexpr int STAGE = WS_OFF + MN * 4;           // 51200 B
+constexpr int P_OFF = NBUF * STAGE;              // route ids: two buffers of 256
+constexpr int B_OFF = P_OFF + 2 * 1024;          // bias: two buffers of 256 fp32
+constexpr int T_OFF = B_OFF + 2 * 1024;          // routing weights: two buffers of 256 fp32
+constexpr int LDS_BYTES = T_OFF + 2 * 1024;      // 156 KiB
+constexpr int GT = 4;                            // tiles sharing the weight blocks on one XCD
+constexpr int MIN_KT = 6;                        // stages per item the ring schedule needs
+
+static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the CU's LDS");
+
+// LDS-DMA loads a wavefront issues per stage: activations 8, their scales 1,
+// weights 4, their scales 1, the next tile's route ids 1, bias 1, routing
+// weights 1
+template <bool BIAS, bool TOPW>
+constexpr int dma_per_stage() { return 15 + (BIAS ? 1 : 0) + (TOPW ? 1 : 0); }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8); counters not named are not waited for
@@ -85,7 +105,7 @@ struct MArgs {
   const float* bias;      // NULL, or fp32 [E, 2I] (GEMM1: gate then up) / [E, H] (GEMM2)
   int K;
   int rows_per_expert;
-  int I;
+  int I;                // GEMM1: row pairs per expert
   int n_out;
   int n_blocks;         // weight-row blocks of 256 (GEMM1: 128 gate + 128 up)
   const int32_t* p2e;
@@ -103,10 +123,12 @@ struct MArgs {
 
 // one LDS-DMA load: lane i moves `bytes` from g to base + bytes * i (base is
 // wave-uniform)
-DEV void dma16(const uint8_t* g, uint8_t* base) {
+DEV void dma16(const void* g, uint8_t* base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)base, 16, 0, 0);
 }
-DEV void dma4(const uint8_t* g, uint8_t* base) { __builtin_amdgcn_global_load_lds(g, (lds_void_t*)base, 4, 0, 0); }
+DEV void dma4(const void* g, uint8_t* base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)base, 4, 0, 0);
+}
 
 // workgroup barrier over LDS that waits for this wave's LDS reads only (no
 // release fence: it would also wait for every LDS-DMA load in flight)
@@ -117,260 +139,599 @@ DEV void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One 32-column MXFP8 block of a y1 row (columns cb + r16 and cb + 16 + r16
-// in this lane): the E8M0 scale from the block's 16-lane max, element pairs
-// stored as 16-bit words, the scale by lane 0.
-DEV void put_block(const MArgs& a, uint8_t* Yq, float y0, float y1, int row, int valid, int slot0, int cb, int r16) {
-  const float am = warp_max16(fmaxf(fabsf(y0), fabsf(y1)));
-  const uint32_t code = mx_scale_code(am, 8);
-  const float y0n = __shfl_xor(y0, 1), y1n = __shfl_xor(y1, 1);
-  if (row < valid) {
-    const int64_t slot = slot0 + row;
-    if ((r16 & 1) == 0) {
-      *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + cb + r16) = (uint16_t)f32x2_to_e4m3x2_mx(y0, y0n, code);
-      *reinterpret_cast<uint16_t*>(Yq + slot * a.n_out + cb + 16 + r16) = (uint16_t)f32x2_to_e4m3x2_mx(y1, y1n, code);
-    }
-    if (r16 == 0) a.Y_sf[slot * (a.n_out / 32) + cb / 32] = (uint8_t)code;
+// A copy of v that the compiler cannot see through: index arithmetic built
+// on it is redone where it is used instead of being hoisted out of the
+// loops and kept live (the registers go to the operand fragments).
+DEV int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Word of slot s in a route-id buffer: the ids a lane's 8 activation loads
+// need are 8 consecutive words (wave w, lane group g = lane >> 3: slots
+// 64 w + 8 j + g at word 64 w + 8 g + j).
+DEV int p_word(int s) { return (s >> 6) * 64 + (s & 7) * 8 + ((s >> 3) & 7); }
+
+// Output column (0..31) that MFMA row i of a tile stands for: lane half h,
+// element j of the 32x32 result holds row 8 (j / 4) + 4 h + j % 4, which is
+// column 16 h + j.
+DEV int tile_col(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+// Row, inside its expert, of weight-row position b (0..255) of block nb.
+template <int GEMM>
+DEV int weight_row(const MArgs& a, int nb, int b) {
+  const int col = tile_col(b & 31);
+  if constexpr (GEMM == 1) {
+    const int m = (b >> 5) & 3;
+    const int c = nb * 128 + 64 * (b >> 7) + 32 * (m & 1) + col;
+    return m < 2 ? c : a.I + c;
+  } else {
+    return nb * MN + (b & ~31) + col;
   }
 }
 
-template <int GEMM, bool ATOMIC, int AK, bool BIAS2>
-DEV void item(const MArgs& a, uint8_t* smem, int e, int slot0, int valid, int nb) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int r16 = lane & 15, q = lane >> 4;
-  const int KT = a.K / MK;
+// A work item's wave-uniform facts: plan tile, weight-row block, local
+// expert, routes in the tile.
+struct Item {
+  int pt, nb, e, valid;
+};
 
-  // ---- sources of this lane's LDS-DMA loads (the stage's K offset is added per stage)
-  // activation row of tile slot s: the token's x row (GEMM1) or the slot's y1 row;
-  // slots past the routes load the first route's row (their results are not stored)
-  const int32_t first = a.p2e[slot0];
-  auto arow = [&](int s) -> int64_t {
-    if constexpr (GEMM == 1) return (int64_t)((s < valid ? a.p2e[slot0 + s] : first) / a.top_k);
-    return (int64_t)(slot0 + min(s, valid - 1));
+// Per-lane 32-bit source offsets of one item's loads (the stage's K offset
+// goes into the wave-uniform base).
+struct Src {
+  uint32_t x[8], xs, w[4], ws, tw;
+};
+
+// Fragments of one 64-K half stage: weight tiles m (this lane's row, K half
+// h: 32 E2M1 codes) and slot tiles n (32 E4M3 codes in two pieces).
+struct Frag {
+  u32x4_t w[4];
+  u32x4_t x[4][2];
+};
+struct Scales {
+  u32x4_t w, x;  // scale words: weight tile m / slot tile n, 4 blocks of 32 K each
+};
+
+// A wave-uniform load through the scalar cache.  Through the constant
+// address space, so the compiler does not fall back to a vector load (whose
+// wait would also wait for every DMA in flight) when the kernel's stores
+// might alias; none of the values read this way is written by the kernel.
+template <typename T>
+DEV T ld_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+DEV Item load_item(const MArgs& a, int pt, int nb) {
+  Item it;
+  it.pt = pt;
+  it.nb = nb;
+  it.e = ld_uniform(a.tile_expert + pt);
+  it.valid = min(MS, ld_uniform(a.tile_limit + pt) - pt * MS);
+  return it;
+}
+
+// Source offsets of an item; its route ids are in buffer P.
+template <int GEMM, bool TOPW>
+DEV Src sources(const MArgs& a, const Item& it, const uint8_t* P, int wave, int lane_) {
+  const int lane = opaque(lane_);
+  Src s;
+  const int g = lane >> 3;
+  auto row_of = [&](int slot, int32_t route) -> int64_t {
+    if constexpr (GEMM == 1) return (int64_t)(route / a.top_k);
+    return (int64_t)it.pt * MS + min(slot, it.valid - 1);
   };
-  // weight row of local row b (0..255) of this block
-  auto wrow = [&](int b) -> int64_t {
-    if constexpr (GEMM == 1) {
-      const int w = b >> 7, j = b & 127;
-      const int col = nb * 128 + 64 * w + (j & 63);
-      return (int64_t)e * a.rows_per_expert + (j < 64 ? col : a.I + col);
-    } else {
-      return (int64_t)e * a.rows_per_expert + nb * MN + b;
+  int32_t rt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int32_t first = 0, rts = 0;
+  const int p = 64 * wave + lane;
+  const int sslot = 128 * (p >> 7) + 32 * (p & 3) + ((p >> 2) & 31);  // slot of this lane's scale word
+  if constexpr (GEMM == 1) {
+    const u32x4_t r0 = *reinterpret_cast<const u32x4_t*>(P + 4 * (64 * wave + 8 * g));
+    const u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(P + 4 * (64 * wave + 8 * g) + 16);
+    first = *reinterpret_cast<const int32_t*>(P);
+    rts = *reinterpret_cast<const int32_t*>(P + 4 * p_word(sslot));
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      rt[j] = (int32_t)r0[j];
+      rt[4 + j] = (int32_t)r1[j];
     }
-  };
-  const uint8_t* a_src[8];
+  }
 #pragma unroll
   for (int j = 0; j < 8; j++) {
-    const int s = 64 * wave + 8 * j + (lane >> 3);         // slot of LDS position 64 (8 wave + j) + lane
-    const int c = (lane & 7) ^ ((s >> 1) & 7);              // logical chunk stored there
-    a_src[j] = a.A + arow(s) * a.a_row_bytes + 16 * c;
+    const int slot = 64 * wave + 8 * j + g;
+    const int c = (lane & 7) ^ ((slot >> 1) & 7);  // logical chunk of physical chunk lane & 7
+    const int64_t row = row_of(slot, slot < it.valid ? rt[j] : first);
+    s.x[j] = (uint32_t)(row * a.a_row_bytes + 16 * c);
   }
-  const uint8_t* as_src;
-  {
-    const int p = 64 * wave + lane;                          // scale word position [wm][r16][m]
-    const int s = 128 * (p >> 7) + 16 * (p & 7) + ((p >> 3) & 15);
-    as_src = a.A_sf + arow(s) * a.a_sf_row;
-  }
-  const uint8_t* b_src[4];
+  s.xs = (uint32_t)(row_of(sslot, sslot < it.valid ? rts : first) * a.a_sf_row);
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int b = 64 * wave + 16 * j + (lane >> 2);
     const int c = (lane & 3) ^ ((b >> 2) & 3);
-    b_src[j] = a.W + wrow(b) * (a.K / 2) + 16 * c;
+    s.w[j] = (uint32_t)(weight_row<GEMM>(a, it.nb, b) * (a.K / 2) + 16 * c);
   }
-  const uint8_t* bs_src;
-  {
-    const int p = 64 * wave + lane;
-    const int b = 128 * (p >> 7) + 16 * (p & 7) + ((p >> 3) & 15);
-    bs_src = a.W_sf + wrow(b) * (a.K / 32);
+  s.ws = (uint32_t)(weight_row<GEMM>(a, it.nb, sslot) * (a.K / 32));
+  // routing weight of slot p (padding slots load entry 0; it is not used)
+  s.tw = 0;
+  if constexpr (TOPW) s.tw = 4u * (uint32_t)max(0, *reinterpret_cast<const int32_t*>(P + 4 * p_word(p)));
+  return s;
+}
+
+// Where a stage's loads go and what the per-item extras are.
+struct Dst {
+  const uint8_t *xb, *xsb, *wb, *wsb;  // the stage's sources: activations, their scales, weights, theirs
+  uint8_t* st;              // stage buffer
+  const int32_t* p2e_tile;  // next tile's route ids -> P
+  uint8_t* P;
+  const float* bias;        // next item's 256 bias values (BIAS) -> B
+  uint8_t* B;
+  uint8_t* T;               // routing weights of the sources' item (TOPW)
+};
+
+// Sources of the stage at K offset k0 of item it.
+DEV void stage_bases(const MArgs& a, const Item& it, int k0, Dst& d) {
+  const int64_t wrow0 = (int64_t)it.e * a.rows_per_expert;
+  d.xb = a.A + k0;
+  d.xsb = a.A_sf + k0 / 32;
+  d.wb = a.W + wrow0 * (a.K / 2) + k0 / 2;
+  d.wsb = a.W_sf + wrow0 * (a.K / 32) + k0 / 32;
+}
+
+template <bool BIAS, bool TOPW>
+DEV void issue(const MArgs& a, const Dst& d, const Src& s, uint32_t p_lane, uint32_t b_lane, int wave) {
+  const uint8_t *xb = d.xb, *xsb = d.xsb, *wb = d.wb, *wsb = d.wsb;
+#pragma unroll
+  for (int j = 0; j < 8; j++) dma16(xb + s.x[j], d.st + X_OFF + 1024 * (8 * wave + j));
+  dma4(xsb + s.xs, d.st + XS_OFF + 256 * wave);
+#pragma unroll
+  for (int j = 0; j < 4; j++) dma16(wb + s.w[j], d.st + W_OFF + 1024 * (4 * wave + j));
+  dma4(wsb + s.ws, d.st + WS_OFF + 256 * wave);
+  dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + p_lane, d.P + 256 * wave);
+  if constexpr (BIAS) dma4(reinterpret_cast<const uint8_t*>(d.bias) + b_lane, d.B + 256 * wave);
+  if constexpr (TOPW) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + s.tw, d.T + 256 * wave);
+}
+
+DEV void read_frag(const uint8_t* st, int wo, int xa, int xb, Frag& f) {
+#pragma unroll
+  for (int m = 0; m < 4; m++) f.w[m] = *reinterpret_cast<const u32x4_t*>(st + wo + 2048 * m);
+#pragma unroll
+  for (int n = 0; n < 4; n++) {
+    f.x[n][0] = *reinterpret_cast<const u32x4_t*>(st + xa + 4096 * n);
+    f.x[n][1] = *reinterpret_cast<const u32x4_t*>(st + xb + 4096 * n);
   }
-  auto issue = [&](int s) {
-    uint8_t* st = smem + (s % NBUF) * STAGE;
-    const int k0 = s * MK;
-#pragma unroll
-    for (int j = 0; j < 8; j++) dma16(a_src[j] + k0, st + A_OFF + 1024 * (8 * wave + j));
-    dma4(as_src + k0 / 32, st + AS_OFF + 256 * wave);
-#pragma unroll
-    for (int j = 0; j < 4; j++) dma16(b_src[j] + k0 / 2, st + B_OFF + 1024 * (4 * wave + j));
-    dma4(bs_src + k0 / 32, st + BS_OFF + 256 * wave);
-  };
+}
 
-  // rows tiles of this wavefront that hold routes
-  const int mt = __builtin_amdgcn_readfirstlane(min(8, max(0, (valid - 128 * wm + 15) >> 4)));
-
-  f32x4_t acc[8][8];
+DEV void mfma_half(f32x16_t (&acc)[4][4], const Frag& f, const Scales& sc, int sh) {
+  int ws[4], xs[4];
 #pragma unroll
-  for (int m = 0; m < 8; m++)
-#pragma unroll
-    for (int n = 0; n < 8; n++) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // every wave of the previous item has read its last stage
-  ring_barrier();
-  issue(0);
-  if (KT > 1) issue(1);
-
-  const int a_sw = (r16 >> 1) & 7;  // activation chunk swizzle of this lane's rows
-  const int b_sw = (r16 >> 2) & 3;  // weight chunk swizzle
-#pragma unroll 1
-  for (int s = 0; s < KT; s++) {
-    // this wave's loads of stage s are done once at most the next stage's are in flight
-    if (s + 1 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_STAGE));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    ring_barrier();
-    if (s + 2 < KT) issue(s + 2);
-    {
-      // the stage's operands: all fragment reads go out before the first
-      // MFMA (no branch between them, so the waits are per fragment; a
-      // branch around the MFMAs would also cost the accumulators their
-      // registers across the loop)
-      const uint8_t* st = smem + (s % NBUF) * STAGE;
-      const u32x4_t* As = reinterpret_cast<const u32x4_t*>(st + A_OFF);
-      const u32x4_t* Bs = reinterpret_cast<const u32x4_t*>(st + B_OFF);
-      const u32x4_t* ASw = reinterpret_cast<const u32x4_t*>(st + AS_OFF + (128 * wm + 8 * r16) * 4);
-      const u32x4_t* BSw = reinterpret_cast<const u32x4_t*>(st + BS_OFF + (128 * wn + 8 * r16) * 4);
-      const u32x4_t as0 = ASw[0], as1 = ASw[1];
-      const u32x4_t bs0 = BSw[0], bs1 = BSw[1];
-      i32x8_t bf[8];
-#pragma unroll
-      for (int n = 0; n < 8; n++) {
-        const int b = 128 * wn + 16 * n + r16;
-        const u32x4_t v = Bs[b * 4 + (q ^ b_sw)];
-        bf[n] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-      }
-      i32x8_t af[8];
-#pragma unroll
-      for (int m = 0; m < 8; m++) {
-        const int row = 128 * wm + 16 * m + r16;
-        const u32x4_t lo = As[row * 8 + (q ^ a_sw)];
-        const u32x4_t hi = As[row * 8 + ((4 + q) ^ a_sw)];
-        af[m] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-#pragma unroll
-      for (int m = 0; m < 8; m++) {
-        const uint32_t aw = m < 4 ? as0[m] : as1[m - 4];
-        const int asc = (int)((aw >> (8 * q)) & 255u);
-#pragma unroll
-        for (int n = 0; n < 8; n++) {
-          const uint32_t bw = n < 4 ? bs0[n] : bs1[n - 4];
-          const int bsc = (int)((bw >> (8 * q)) & 255u);
-          acc[m][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[m], bf[n], acc[m][n], 0, 4, 0, asc, 0, bsc);
-        }
-      }
-    }
+  for (int i = 0; i < 4; i++) {
+    ws[i] = (int)((sc.w[i] >> sh) & 255u);
+    xs[i] = (int)((sc.x[i] >> sh) & 255u);
   }
-
-  // ---- epilogue.  Lane holds slots 128 wm + 16 m + 4 q + i, column r16 of each tile.
-  const float alpha = a.alpha[e];
-  if constexpr (GEMM == 1) {
-    const float alpha_u = a.alpha_up ? a.alpha_up[e] : alpha;
-    const int col0 = nb * 128 + 64 * wn;  // this wave's 64 y1 columns (gate tiles n = 0..3, up n + 4)
-    uint8_t* Yq = reinterpret_cast<uint8_t*>(a.Y);
 #pragma unroll
-    for (int m = 0; m < 8; m++) {
-      if (m >= mt) continue;
+  for (int m = 0; m < 4; m++) {
+    const i32x8_t av = {(int)f.w[m][0], (int)f.w[m][1], (int)f.w[m][2], (int)f.w[m][3], 0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int row = 128 * wm + 16 * m + 4 * q + i;
-#pragma unroll
-        for (int bb = 0; bb < 2; bb++) {  // y1 block of 32 columns: tiles 2 bb, 2 bb + 1
-          float y[2], z[2];
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-            const int n = 2 * bb + h;
-            float g = acc[m][n][i] * alpha;
-            float u = acc[m][n + 4][i] * alpha_u;
-            if (a.bias) {
-              g = g + a.bias[(int64_t)e * 2 * a.I + col0 + 16 * n + r16];
-              u = u + a.bias[(int64_t)e * 2 * a.I + a.I + col0 + 16 * n + r16];
-            }
-            // y1 is rounded once to bf16; requantisation starts from that value
-            if constexpr (AK == ACT_RELU2) {
-              y[h] = bf16_to_f32(f32_to_bf16(relu2_f32(g)));
-              z[h] = bf16_to_f32(f32_to_bf16(relu2_f32(u)));
-            } else {
-              y[h] = bf16_to_f32(f32_to_bf16(gated_act_k<AK>(g, u, a.act)));
-            }
-          }
-          put_block(a, Yq, y[0], y[1], row, valid, slot0, col0 + 32 * bb, r16);
-          if constexpr (AK == ACT_RELU2) put_block(a, Yq, z[0], z[1], row, valid, slot0, a.I + col0 + 32 * bb, r16);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int m = 0; m < 8; m++) {
-      if (m >= mt) continue;
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int row = 128 * wm + 16 * m + 4 * q + i;
-        if constexpr (!ATOMIC) {
-          uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
-          if (row < valid) {
-#pragma unroll
-            for (int n = 0; n < 8; n++) {
-              const int col = nb * MN + 128 * wn + 16 * n + r16;
-              float v = acc[m][n][i] * alpha;
-              if constexpr (BIAS2) v = v + a.bias[(int64_t)e * a.n_out + col];
-              Y[(int64_t)(slot0 + row) * a.n_out + col] = f32_to_bf16(v);
-            }
-          }
-        } else {
-          const int32_t route = (row < valid) ? a.p2e[slot0 + row] : -1;
-          const float wf = (route >= 0) ? __fmul_rn(a.topk_w[route], a.rsf) : 0.0f;
-#pragma unroll
-          for (int n = 0; n < 8; n++) {
-            const int col = nb * MN + 128 * wn + 16 * n + r16;
-            float v = acc[m][n][i] * alpha;
-            if constexpr (BIAS2) v = v + a.bias[(int64_t)e * a.n_out + col];
-            const float y2 = bf16_to_f32(f32_to_bf16(v));
-            const float c = __fmul_rn(wf, y2);
-            const float cn = __shfl_xor(c, 1);
-            if (route >= 0 && (r16 & 1) == 0) {
-              const int64_t t = route / a.top_k;
-              bf16x2_t v2 = {(__bf16)c, (__bf16)cn};
-              __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<bf16x2_t*>(a.out + t * a.n_out + col), v2);
-            }
-          }
-        }
-      }
+    for (int n = 0; n < 4; n++) {
+      const i32x8_t bv = {(int)f.x[n][0][0], (int)f.x[n][0][1], (int)f.x[n][0][2], (int)f.x[n][0][3],
+                          (int)f.x[n][1][0], (int)f.x[n][1][1], (int)f.x[n][1][2], (int)f.x[n][1][3]};
+      acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[m][n], 4, 0, 0, ws[m], 0, xs[n]);
     }
   }
 }
 
-template <int GEMM, bool ATOMIC, int AK, bool BIAS2>
+// Per-lane LDS offsets of the fragment reads (swizzled chunks, see
+// sources) and of the per-item loads; recomputed for every item from an
+// opaque lane id, so that none of them is live across the epilogue.
+struct LaneOffs {
+  int wo0, wo1, xo0, xo1, xo2, xo3, wso, xso, sh0, sh1;
+  uint32_t p_lane, b_lane;
+};
+
+template <int GEMM>
+DEV LaneOffs lane_offsets(const MArgs& a, int wave, int lane_) {
+  const int lane = opaque(lane_);
+  const int ww = wave & 1, ws = wave >> 1;
+  const int r = lane & 31, h = lane >> 5;
+  LaneOffs L;
+  const int wrow = W_OFF + (128 * ww + r) * (MK / 2), wsw = (r >> 2) & 3;
+  L.wo0 = wrow + 16 * (h ^ wsw);
+  L.wo1 = wrow + 16 * ((2 + h) ^ wsw);
+  const int xrow = X_OFF + (128 * ws + r) * MK, xsw = (r >> 1) & 7;
+  L.xo0 = xrow + 16 * (h ^ xsw);
+  L.xo1 = xrow + 16 * ((2 + h) ^ xsw);
+  L.xo2 = xrow + 16 * ((4 + h) ^ xsw);
+  L.xo3 = xrow + 16 * ((6 + h) ^ xsw);
+  L.wso = WS_OFF + (32 * ww + r) * 16;
+  L.xso = XS_OFF + (32 * ws + r) * 16;
+  L.sh0 = 8 * h;  // scale byte of block 2 u + h
+  L.sh1 = 16 + 8 * h;
+  // route-id load: position 64 wave + lane holds slot 64 wave + 8 (lane & 7)
+  // + (lane >> 3); bias load: value 64 wave + lane (GEMM1: gate columns
+  // 0..127 of the block, then the up half)
+  L.p_lane = 4u * (uint32_t)(64 * wave + 8 * (lane & 7) + (lane >> 3));
+  const int bpos = 64 * wave + lane;
+  L.b_lane = 4u * (uint32_t)(GEMM == 1 && bpos >= 128 ? a.I + bpos - 128 : bpos);
+  return L;
+}
+
+// Second half of a stage, written in issue order: load i of the stage,
+// MFMA i on the second-half fragments f1, read i of the next stage's first
+// half into f0 / scn (READS; an item's last stage leaves them to after the
+// epilogue, which then has their registers).  (LDS-DMA loads are scheduling boundaries, so the
+// interleave is set here rather than left to the scheduler.)
+template <int NDMA, bool BIAS, bool TOPW, bool READS>
+DEV void second_half(const MArgs& a, f32x16_t (&acc)[4][4], const Frag& f1, const Scales& sc, const Dst& d,
+                     const Src& s, const LaneOffs& L, int wave, const uint8_t* stn, Frag& f0, Scales& scn) {
+  const uint8_t *xb = d.xb, *xsb = d.xsb, *wb = d.wb, *wsb = d.wsb;
+  int wsc[4], xsc[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    wsc[i] = (int)((sc.w[i] >> L.sh1) & 255u);
+    xsc[i] = (int)((sc.x[i] >> L.sh1) & 255u);
+  }
+#pragma unroll
+  for (int i = 0; i < 17; i++) {
+    if (i < NDMA) {
+      if (i < 8) dma16(xb + s.x[i], d.st + X_OFF + 1024 * (8 * wave + i));
+      else if (i == 8) dma4(xsb + s.xs, d.st + XS_OFF + 256 * wave);
+      else if (i < 13) dma16(wb + s.w[i - 9], d.st + W_OFF + 1024 * (4 * wave + i - 9));
+      else if (i == 13) dma4(wsb + s.ws, d.st + WS_OFF + 256 * wave);
+      else if (i == 14) dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + L.p_lane, d.P + 256 * wave);
+      else if (i == 15 && BIAS) dma4(reinterpret_cast<const uint8_t*>(d.bias) + L.b_lane, d.B + 256 * wave);
+      else if (TOPW) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + s.tw, d.T + 256 * wave);
+    }
+    if (i < 16) {
+      const int m = i >> 2, n = i & 3;
+      const i32x8_t av = {(int)f1.w[m][0], (int)f1.w[m][1], (int)f1.w[m][2], (int)f1.w[m][3], 0, 0, 0, 0};
+      const i32x8_t bv = {(int)f1.x[n][0][0], (int)f1.x[n][0][1], (int)f1.x[n][0][2], (int)f1.x[n][0][3],
+                          (int)f1.x[n][1][0], (int)f1.x[n][1][1], (int)f1.x[n][1][2], (int)f1.x[n][1][3]};
+      acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[m][n], 4, 0, 0, wsc[m], 0, xsc[n]);
+    }
+    if (!READS) continue;
+    if (i == 0) scn.w = *reinterpret_cast<const u32x4_t*>(stn + L.wso);
+    else if (i == 1) scn.x = *reinterpret_cast<const u32x4_t*>(stn + L.xso);
+    else if (i < 6) f0.w[i - 2] = *reinterpret_cast<const u32x4_t*>(stn + L.wo0 + 2048 * (i - 2));
+    else if (i < 14) {
+      const int n = (i - 6) >> 1, piece = (i - 6) & 1;
+      f0.x[n][piece] = *reinterpret_cast<const u32x4_t*>(stn + (piece ? L.xo1 : L.xo0) + 4096 * n);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Instruction order of a stage's first half for the scheduler (groups:
+// 0x008 MFMA, 0x100 LDS read): its 12 fragment reads between the first 12
+// MFMAs.
+DEV void order_first_half() {
+#pragma unroll
+  for (int i = 0; i < 12; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+// SwiGLU of one gate/up pair with the hardware exp2 and reciprocal (a few
+// fp32 ulps, against the MFMA's own accumulation error of about 2^-21 of
+// the sum): min(g, l) * sigmoid(alpha * min(g, l)) * (clamp(u, -l, l) + beta).
+DEV float swiglu_fast(float g, float u, const GateAct& p) {
+  const float gc = fminf(g, p.limit);
+  const float uc = fminf(fmaxf(u, -p.limit), p.limit);
+  const float e = __builtin_amdgcn_exp2f(-p.alpha * 1.4426950408889634f * gc);
+  return gc * __builtin_amdgcn_rcpf(1.0f + e) * (uc + p.beta);
+}
+
+template <int AK>
+DEV float act_value(float g, float u, const GateAct& p) {
+  if constexpr (AK == ACT_SWIGLU) return swiglu_fast(g, u, p);
+  else return gated_act_k<AK>(g, u, p);
+}
+
+DEV float bf16_round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+
+// 16 consecutive fp32 values from LDS
+DEV void lds16(const uint8_t* p, float (&v)[16]) {
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const u32x4_t q = reinterpret_cast<const u32x4_t*>(p)[k];
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[4 * k + i] = __uint_as_float(q[i]);
+  }
+}
+
+// One 32-column MXFP8 block of a y1 row: this lane holds 16 consecutive
+// columns (from `col`), lane ^ 32 the other 16.  The block max decides the
+// E8M0 code; values are clamped to the code's E4M3 range and converted in
+// fours; half h = 0 writes the scale byte.
+DEV void put_block16(const MArgs& a, const float (&y)[16], int64_t yrow, int col, bool ok, int h) {
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(y[j]));
+  am = fmaxf(am, __shfl_xor(am, 32));
+  const uint32_t code = mx_scale_code(am, 8);
+  const float lim = __builtin_ldexpf(448.0f, (int)code - 127);
+  const float sc = e8m0_scale_operand(code);
+  u32x4_t q;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = fminf(fmaxf(y[4 * k + i], -lim), lim);
+    i16x2_t r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, v[0], v[1], sc, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, v[2], v[3], sc, true);
+    q[k] = __builtin_bit_cast(uint32_t, r);
+  }
+  if (ok) {
+    uint8_t* Yq = reinterpret_cast<uint8_t*>(a.Y);
+    *reinterpret_cast<u32x4_t*>(Yq + yrow * a.n_out + col) = q;
+    if (h == 0) a.Y_sf[yrow * (a.n_out / 32) + col / 32] = (uint8_t)code;
+  }
+}
+
+// GEMM1 epilogue; Bv: the item's bias (gate columns, then up columns)
+template <int AK, bool BIAS>
+DEV void epilogue1(const MArgs& a, const f32x16_t (&acc)[4][4], const Item& it, const uint8_t* Bv, int ww, int ws,
+                   int lane_) {
+  const int lane = opaque(lane_);
+  const int r = lane & 31, h = lane >> 5;
+  const float alpha = ld_uniform(a.alpha + it.e);
+  const float alpha_u = a.alpha_up ? ld_uniform(a.alpha_up + it.e) : alpha;
+#pragma unroll
+  for (int m = 0; m < 2; m++) {
+    const int lc = 64 * ww + 32 * m + 16 * h;  // this lane's first column inside the block
+    const int col = it.nb * 128 + lc;
+    float bg[16], bu[16];
+    if constexpr (BIAS) {
+      lds16(Bv + 4 * lc, bg);
+      lds16(Bv + 4 * (128 + lc), bu);
+    }
+#pragma unroll
+    for (int n = 0; n < 4; n++) {
+      const int slot = 128 * ws + 32 * n + r;
+      const bool ok = slot < it.valid;
+      const int64_t yrow = (int64_t)it.pt * MS + slot;
+      float y[16], z[16];
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        float g = acc[m][n][j] * alpha;
+        float u = acc[m + 2][n][j] * alpha_u;
+        if constexpr (BIAS) {
+          g = g + bg[j];
+          u = u + bu[j];
+        }
+        // y1 is rounded once to bf16; requantisation starts from that value
+        if constexpr (AK == ACT_RELU2) {
+          y[j] = bf16_round(relu2_f32(g));
+          z[j] = bf16_round(relu2_f32(u));
+        } else {
+          y[j] = bf16_round(act_value<AK>(g, u, a.act));
+        }
+      }
+      put_block16(a, y, yrow, col, ok, h);
+      if constexpr (AK == ACT_RELU2) put_block16(a, z, yrow, a.I + col, ok, h);
+      // one block at a time: keeps the accumulator reads from being hoisted
+      // in bulk into registers the fragments hold
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// GEMM2 epilogue; P, Bv, Tw: the item's route ids, bias, routing weights
+template <bool ATOMIC, bool BIAS>
+DEV void epilogue2(const MArgs& a, const f32x16_t (&acc)[4][4], const Item& it, const uint8_t* P, const uint8_t* Bv,
+                   const uint8_t* Tw, int ww, int ws, int lane_) {
+  const int lane = opaque(lane_);
+  const int r = lane & 31, h = lane >> 5;
+  const float alpha = ld_uniform(a.alpha + it.e);
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const int lc = 128 * ww + 32 * m + 16 * h;
+    const int col = it.nb * MN + lc;
+    float bv[16];
+    if constexpr (BIAS) lds16(Bv + 4 * lc, bv);
+#pragma unroll
+    for (int n = 0; n < 4; n++) {
+      const int slot = 128 * ws + 32 * n + r;
+      const bool ok = slot < it.valid;
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        v[j] = acc[m][n][j] * alpha;
+        if constexpr (BIAS) v[j] = v[j] + bv[j];
+      }
+      if constexpr (!ATOMIC) {
+        u32x4_t lo, hi;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          lo[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
+          hi[k] = (uint32_t)f32_to_bf16(v[8 + 2 * k]) | ((uint32_t)f32_to_bf16(v[8 + 2 * k + 1]) << 16);
+        }
+        if (ok) {
+          uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y) + ((int64_t)it.pt * MS + slot) * a.n_out + col;
+          reinterpret_cast<u32x4_t*>(Y)[0] = lo;
+          reinterpret_cast<u32x4_t*>(Y)[1] = hi;
+        }
+      } else {
+        const int32_t route = ok ? *reinterpret_cast<const int32_t*>(P + 4 * p_word(slot)) : -1;
+        if (route >= 0) {
+          const float wf = __fmul_rn(*reinterpret_cast<const float*>(Tw + 4 * slot), a.rsf);
+          uint16_t* o = a.out + (int64_t)(route / a.top_k) * a.n_out + col;
+#pragma unroll
+          for (int k = 0; k < 8; k++) {
+            const float c0 = __fmul_rn(wf, bf16_round(v[2 * k]));
+            const float c1 = __fmul_rn(wf, bf16_round(v[2 * k + 1]));
+            bf16x2_t v2 = {(__bf16)c0, (__bf16)c1};
+            __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<bf16x2_t*>(o + 2 * k), v2);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int GEMM, bool ATOMIC, int AK, bool BIAS>
 __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  // A persistent grid: K blocks per XCD, block b on XCD b & 7 (workgroups
-  // are dealt to the XCDs round-robin).  Tiles go in groups of GT
-  // consecutive ranks of the heaviest-first order (tiles of one expert,
-  // mostly), group g to XCD g & 7.  An XCD's K blocks take its items in
-  // order, and a group's items are ordered in passes of K / GT weight-row
-  // blocks, the GT tiles' items of one block next to each other: the K
-  // concurrent items of an XCD then share each weight block among GT tiles
-  // and each tile's activation rows among K / GT weight blocks, in that
-  // XCD's L2.
-  const int T = *a.num_tiles;
-  const int x = blockIdx.x & 7;
-  const int K = gridDim.x >> 3;
+  constexpr bool TOPW = GEMM == 2 && ATOMIC;
+  constexpr int NDMA = dma_per_stage<BIAS, TOPW>();
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ww = wave & 1, ws = wave >> 1;
+  const int KT = a.K / MK;
+
+  // A persistent grid: KB workgroups per XCD, workgroup b on XCD b & 7
+  // (workgroups are dealt to the XCDs round-robin).  Tiles go in groups of
+  // GT consecutive plan tiles, group g to XCD g & 7.  An XCD's workgroups
+  // take its items in order, and a group's items are ordered in passes of
+  // KB / GT weight-row blocks, the GT tiles' items of one block next to each
+  // other: the KB concurrent items of an XCD then share each weight block
+  // among GT tiles and each tile's activation rows among KB / GT weight
+  // blocks, in that XCD's L2.
+  const int T = ld_uniform(a.num_tiles);
+  const int xcd = blockIdx.x & 7;
+  const int KB = gridDim.x >> 3;
   const int G = (T + GT - 1) / GT;
   const int per_group = GT * a.n_blocks;
-  const int pw = max(1, min(a.n_blocks, K / GT));  // weight-row blocks per pass
-  for (int j = blockIdx.x >> 3;; j += K) {
-    const int g = x + 8 * (j / per_group);
-    if (g >= G) return;
-    const int idx = j % per_group;
-    const int pass = idx / (GT * pw);
-    const int in = idx % (GT * pw);
-    const int nb = pass * pw + in / GT;
-    const int r = GT * g + in % GT;
-    if (r >= T || nb >= a.n_blocks) continue;
-    const int pt = tile_of_rank(a.tile_limit, T, MS, r, MT);
-    const int e = __builtin_amdgcn_readfirstlane(a.tile_expert[pt]);
-    const int slot0 = pt * MS;
-    const int valid = __builtin_amdgcn_readfirstlane(min(MS, a.tile_limit[pt] - slot0));
-    item<GEMM, ATOMIC, AK, BIAS2>(a, smem, e, slot0, valid, nb);
+  const int pw = max(1, min(a.n_blocks, KB / GT));
+  // first item at or after position j of this XCD's sequence; -1: none
+  auto find = [&](int j, int& pt, int& nb) -> int {
+    for (;; j += KB) {
+      const int g = xcd + 8 * (j / per_group);
+      if (g >= G) return -1;
+      const int idx = j % per_group;
+      const int in = idx % (GT * pw);
+      nb = (idx / (GT * pw)) * pw + in / GT;
+      pt = GT * g + in % GT;
+      if (pt < T && nb < a.n_blocks) return j;
+    }
+  };
+  // the item's 256 bias values: GEMM1 128 gate then 128 up columns of its
+  // block, GEMM2 its 256 output columns
+  auto bias_of = [&](const Item& it) -> const float* {
+    if constexpr (GEMM == 1) return a.bias + (int64_t)it.e * 2 * a.I + it.nb * 128;
+    return a.bias + (int64_t)it.e * a.n_out + it.nb * MN;
+  };
+
+  int cpt = 0, cnb = 0;
+  int cj = find(blockIdx.x >> 3, cpt, cnb);
+  if (cj < 0) return;
+  Item cur = load_item(a, cpt, cnb);
+  int npt = cpt, nnb = cnb;
+  int nj = find(cj + KB, npt, nnb);
+  Item nxt = nj >= 0 ? load_item(a, npt, nnb) : cur;
+
+  auto Pb = [&](int i) -> uint8_t* { return smem + P_OFF + i * 1024; };
+  auto Bb = [&](int i) -> uint8_t* { return smem + B_OFF + i * 1024; };
+  auto Tb = [&](int i) -> uint8_t* { return smem + T_OFF + i * 1024; };
+  int pb = 0;
+
+  // route ids (and bias) of the first item, then its sources
+  {
+    const LaneOffs L0 = lane_offsets<GEMM>(a, wave, lane);
+    dma4(reinterpret_cast<const uint8_t*>(a.p2e + (int64_t)cur.pt * MS) + L0.p_lane, Pb(0) + 256 * wave);
+    if constexpr (BIAS) dma4(reinterpret_cast<const uint8_t*>(bias_of(cur)) + L0.b_lane, Bb(0) + 256 * wave);
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  ring_barrier();
+  Src cs = sources<GEMM, TOPW>(a, cur, Pb(0), wave, lane);
+
+  LaneOffs L = lane_offsets<GEMM>(a, wave, lane);
+
+  // the first three stages; every stage's loads also refresh the next
+  // item's route ids and bias
+  {
+    Dst d;
+    d.p2e_tile = a.p2e + (int64_t)nxt.pt * MS;
+    d.P = Pb(1);
+    d.bias = BIAS ? bias_of(nxt) : nullptr;
+    d.B = Bb(1);
+    d.T = Tb(0);
+#pragma unroll 1
+    for (int s = 0; s < NBUF; s++) {
+      d.st = smem + s * STAGE;
+      stage_bases(a, cur, s * MK, d);
+      issue<BIAS, TOPW>(a, d, cs, L.p_lane, L.b_lane, wave);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));
+  ring_barrier();
+
+  Frag f0, f1;
+  Scales sc, scn;
+
+  f32x16_t acc[4][4];
+  int buf = 0;
+#pragma unroll 1
+  for (;;) {
+    // the first half of the item's first stage (visible since the last
+    // stage's barrier; its buffer is refilled only after the next barrier)
+    L = lane_offsets<GEMM>(a, wave, lane);
+    sc.w = *reinterpret_cast<const u32x4_t*>(smem + buf * STAGE + L.wso);
+    sc.x = *reinterpret_cast<const u32x4_t*>(smem + buf * STAGE + L.xso);
+    read_frag(smem + buf * STAGE, L.wo0, L.xo0, L.xo1, f0);
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+#pragma unroll
+      for (int n = 0; n < 4; n++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[m][n][i] = 0.0f;
+
+    auto stage = [&](int s, auto last_) {
+      constexpr bool last = decltype(last_)::value;
+      const bool same = s + 3 < KT;
+      const int k0 = (same ? s + 3 : s + 3 - KT) * MK;
+      uint8_t* st = smem + buf * STAGE;
+      const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+      const uint8_t* stn = smem + nbuf * STAGE;
+
+      // what this stage loads (scalar work, done among the first half's MFMAs)
+      Dst d;
+      stage_bases(a, same ? cur : nxt, k0, d);
+      d.st = st;
+      d.p2e_tile = a.p2e + (int64_t)nxt.pt * MS;
+      d.P = Pb(pb ^ 1);
+      d.bias = BIAS ? bias_of(nxt) : nullptr;
+      d.B = Bb(pb ^ 1);
+      d.T = Tb(same ? pb : pb ^ 1);
+      // first half: its fragments are in f0; read the second half's
+      read_frag(st, L.wo1, L.xo2, L.xo3, f1);
+      mfma_half(acc, f0, sc, L.sh0);
+      order_first_half();
+      __builtin_amdgcn_sched_barrier(0);
+      // stage + 1 has landed once only the last stage's loads are in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
+      ring_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // every wave is done with this stage's buffer: refill it three stages
+      // on; second half, while the next stage's first half is read
+      second_half<NDMA, BIAS, TOPW, !last>(a, acc, f1, sc, d, cs, L, wave, stn, f0, scn);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!last) sc = scn;
+      buf = nbuf;
+    };
+#pragma unroll 1
+    for (int s = 0; s < KT - 1; s++) {
+      // the next item's sources, once its route ids have landed (the
+      // third stage's wait covered the loads of the first)
+      if (s == KT - 3) cs = sources<GEMM, TOPW>(a, nxt, Pb(pb ^ 1), wave, lane);
+      stage(s, std::false_type{});
+    }
+    stage(KT - 1, std::true_type{});
+
+    if constexpr (GEMM == 1) epilogue1<AK, BIAS>(a, acc, cur, Bb(pb), ww, ws, lane);
+    else epilogue2<ATOMIC, BIAS>(a, acc, cur, Pb(pb), Bb(pb), Tb(pb), ww, ws, lane);
+
+    if (nj < 0) break;
+    cur = nxt;
+    cj = nj;
+    pb ^= 1;
+    nj = find(cj + KB, npt, nnb);
+    if (nj >= 0) nxt = load_item(a, npt, nnb);
+  }
+  // no LDS-DMA load may still be writing when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 void plan_args(MArgs& a, const moe_plan_t* plan) {
@@ -381,9 +742,9 @@ void plan_args(MArgs& a, const moe_plan_t* plan) {
   a.top_k = plan->top_k;
 }
 
-template <int GEMM, bool ATOMIC, int AK, bool BIAS2>
+template <int GEMM, bool ATOMIC, int AK, bool BIAS>
 hipError_t launch_one(const MArgs& a, int max_tiles, hipStream_t s) {
-  auto kern = mxw_gemm_kernel<GEMM, ATOMIC, AK, BIAS2>;
+  auto kern = mxw_gemm_kernel<GEMM, ATOMIC, AK, BIAS>;
   // the launch needs more than the default 64 KiB of dynamic LDS: allow it
   // once per device
   static bool attr[64] = {};
@@ -409,20 +770,26 @@ hipError_t launch_one(const MArgs& a, int max_tiles, hipStream_t s) {
 }
 
 bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+constexpr int64_t OFF_LIMIT = (int64_t)1 << 31;  // the 32-bit lane offsets stay below this
 
 }  // namespace
 
-// 256-slot plan tiles; K a multiple of 128; whole weight-row blocks;
-// 16-byte aligned activation rows; 4-byte aligned scale rows and arrays
+// 256-slot plan tiles; K a multiple of 128 with at least MIN_KT stages;
+// whole weight-row blocks; 16-byte aligned rows; 4-byte aligned scale rows
+// and arrays; every source offset inside 31 bits
 bool mxw_supported1(const Gemm1Params& p) {
   const int64_t stride = p.x_row_stride ? p.x_row_stride : p.H;
-  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == MS && p.H % MK == 0 && gemm1_pairs(p) % 128 == 0 &&
-         stride % 16 == 0 && ((uintptr_t)p.x & 15) == 0 && aligned4(p.x_sf) && aligned4(p.w1_sf) &&
-         aligned4(p.y1_sf) && ((uintptr_t)p.y1 & 1) == 0 && ((uintptr_t)p.w1 & 15) == 0;
+  const int IP = gemm1_pairs(p);
+  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == MS && p.H % MK == 0 && p.H / MK >= MIN_KT &&
+         IP % 128 == 0 && stride % 16 == 0 && ((uintptr_t)p.x & 15) == 0 && aligned4(p.x_sf) &&
+         aligned4(p.w1_sf) && ((uintptr_t)p.y1 & 15) == 0 && ((uintptr_t)p.w1 & 15) == 0 &&
+         (int64_t)p.plan->M * stride < OFF_LIMIT && (int64_t)2 * IP * (p.H / 2) < OFF_LIMIT;
 }
 bool mxw_supported2(const Gemm2Params& p) {
-  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == MS && p.I % MK == 0 && p.H % MN == 0 &&
-         ((uintptr_t)p.y1 & 15) == 0 && aligned4(p.y1_sf) && aligned4(p.w2_sf) && ((uintptr_t)p.w2 & 15) == 0;
+  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == MS && p.I % MK == 0 && p.I / MK >= MIN_KT &&
+         p.H % MN == 0 && ((uintptr_t)p.y1 & 15) == 0 && aligned4(p.y1_sf) && aligned4(p.w2_sf) &&
+         ((uintptr_t)p.w2 & 15) == 0 && (!p.y2 || ((uintptr_t)p.y2 & 15) == 0) &&
+         p.plan->route_slots * p.I < OFF_LIMIT && (int64_t)p.H * (p.I / 2) < OFF_LIMIT;
 }
 
 hipError_t launch_gemm1_mxw(const Gemm1Params& p, hipStream_t stream) {
@@ -447,6 +814,14 @@ hipError_t launch_gemm1_mxw(const Gemm1Params& p, hipStream_t stream) {
   a.Y = p.y1;
   a.Y_sf = p.y1_sf;
   const int mt = p.plan->max_tiles;
+  if (p.fc1_bias) {
+    switch (p.act.kind) {
+      case ACT_GEGLU_TANH: return launch_one<1, false, ACT_GEGLU_TANH, true>(a, mt, stream);
+      case ACT_SITU: return launch_one<1, false, ACT_SITU, true>(a, mt, stream);
+      case ACT_RELU2: return launch_one<1, false, ACT_RELU2, true>(a, mt, stream);
+      default: return launch_one<1, false, ACT_SWIGLU, true>(a, mt, stream);
+    }
+  }
   switch (p.act.kind) {
     case ACT_GEGLU_TANH: return launch_one<1, false, ACT_GEGLU_TANH, false>(a, mt, stream);
     case ACT_SITU: return launch_one<1, false, ACT_SITU, false>(a, mt, stream);

@@ -56,6 +56,17 @@ CASES = {
                                              activation=oracle.ACT_RELU2)),
     "mx_relu2_partial": (oracle.MXFP8_MXFP4, dict(M=300, H=192, I=320, E=8, El=6, k=3, seed=85, offset=1,
                                                   router_bias_std=0.7, activation=oracle.ACT_RELU2)),
+    # K of at least 768 in both GEMMs: with 256-slot tiles the MX mode takes the LDS-DMA ring kernels
+    # (the large-batch shape of pull request 4440's benchmark), here with ragged tiles, an expert
+    # window and every FC1 activation
+    "mx_k768": (oracle.MXFP8_MXFP4, dict(M=300, H=768, I=768, E=8, El=6, k=3, seed=86, offset=1,
+                                         router_bias_std=0.7, swiglu_limit=2.0)),
+    "mx_k768_relu2": (oracle.MXFP8_MXFP4, dict(M=300, H=768, I=1024, E=8, El=6, k=3, seed=87, offset=1,
+                                               router_bias_std=0.7, activation=oracle.ACT_RELU2)),
+    "mx_k768_geglu": (oracle.MXFP8_MXFP4, dict(M=200, H=1024, I=768, E=8, El=8, k=3, seed=88,
+                                               activation=oracle.ACT_GEGLU_TANH)),
+    "mx_k768_situ": (oracle.MXFP8_MXFP4, dict(M=200, H=768, I=768, E=8, El=8, k=3, seed=89, situ_beta=0.1,
+                                              situ_linear_beta=0.08)),
 }
 
 _cache = {}
@@ -172,7 +183,7 @@ def test_atomic_finalize_and_accumulate(name):
 
 
 SCALED = ["w4a16_basic", "w4a16_wide", "w4a16_stream", "w4a4_offset", "w4a4_tall", "mx_tall", "w4a16_partial",
-          "w4a4_partial", "mx_partial"]
+          "w4a4_partial", "mx_partial", "mx_k768"]
 
 
 def scaled_problem(name):
@@ -193,7 +204,7 @@ def scaled_problem(name):
 
 
 @pytest.mark.parametrize("name", SCALED)
-@pytest.mark.parametrize("tile", [0, 16, 128])
+@pytest.mark.parametrize("tile", [0, 16, 128, 256])
 def test_scales_and_routed_scaling(name, tile):
     """The up half's own per-expert scale, the W4A4 per-token input row scale,
     FC1 / FC2 biases and routed_scaling_factor != 1 through every GEMM1 and
@@ -213,6 +224,60 @@ def test_scales_and_routed_scaling(name, tile):
     d.forward(out=out, tile=tile, finalize_mode=moe.FINALIZE_ATOMIC)
     torch.cuda.synchronize()
     check_close(host(out, np.uint16), want, p.mode, f"{name} scaled atomic")
+
+
+@pytest.mark.parametrize("name", ["mx_k768", "mx_k768_relu2", "mx_k768_situ"])
+def test_mx_wide_tile_finalize(name):
+    """256-slot tiles in the MX mode (the LDS-DMA ring kernels, whose GEMM2
+    epilogue also does the atomic finalize): atomic finalize onto garbage,
+    accumulation in both finalize modes."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, check_close, dev, host, say
+    p = problem(name)
+    say(f"MX 256-slot finalize {name}")
+    d = DeviceProblem(p)
+    want = oracle.forward_tokens(p, np.arange(p.M))
+    out = torch.full((p.M, p.H), 0x3f80, dtype=torch.int16, device="cuda")
+    d.forward(out=out, tile=256, finalize_mode=moe.FINALIZE_ATOMIC)
+    torch.cuda.synchronize()
+    check_close(host(out, np.uint16), want, p.mode, f"{name} atomic")
+    prev = synth.normal_bf16(9, 9, (p.M, p.H), 0.0, 0.01)
+    want_acc = oracle.forward_tokens(p, np.arange(p.M), accumulate=True, out_prev=prev)
+    for fm in (moe.FINALIZE_DETERMINISTIC, moe.FINALIZE_ATOMIC):
+        out = dev(prev.copy())
+        d.forward(out=out, tile=256, accumulate=True, finalize_mode=fm)
+        torch.cuda.synchronize()
+        check_close(host(out, np.uint16), want_acc, p.mode, f"{name} accumulate ({fm})")
+
+
+def test_mx_wide_tile_many_items():
+    """Enough 256-slot tiles (64, over 8 experts) that workgroups of the
+    persistent MX kernels take several work items in turn in both GEMMs:
+    the LDS ring runs on from one item into the next, also into another
+    expert's.  Checked on sampled tokens plus the largest outputs, in both
+    finalize modes."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, check_close, host, say
+    wl = synth.small_workload(oracle.MXFP8_MXFP4, 4096, 2048, 768, 8, 8, 4, 90, router_bias_std=0.5)
+    p = oracle.quantize_problem(synth.make_raw(wl))
+    say("MX 256-slot tiles, several items per workgroup")
+    d = DeviceProblem(p)
+    out = d.forward(tile=256)
+    torch.cuda.synchronize()
+    toks = synth.sample_tokens(90, p.M, 160)
+    peak = np.abs(synth.bf16_to_f32(host(out, np.uint16))).max(axis=1)
+    order = np.argsort(-peak, kind="stable")[:64 + toks.size]
+    toks = np.concatenate([toks, order[~np.isin(order, toks)][:64].astype(np.int32)])
+    want = oracle.forward_tokens(p, toks)
+    check_close(host(out, np.uint16)[toks], want, p.mode, "many items")
+    out_a = torch.zeros_like(out)
+    d.forward(out=out_a, tile=256, finalize_mode=moe.FINALIZE_ATOMIC)
+    torch.cuda.synchronize()
+    check_close(host(out_a, np.uint16)[toks], want, p.mode, "many items atomic")
 
 
 def test_row_strided_x():
