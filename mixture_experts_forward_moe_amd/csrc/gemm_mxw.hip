@@ -67,25 +67,27 @@ constexpr int MS = 256;                          // slots per tile
 constexpr int MN = 256;                          // weight rows per item
 constexpr int MK = 128;                          // K per stage
 constexpr int NBUF = 3;                          // stages in the LDS ring
+constexpr int GS = 4;                            // stages per scale group
 constexpr int X_OFF = 0;                         // activations [256 slots][8 chunks of 16 B]
-constexpr int XS_OFF = MS * MK;                  // activation scale words
-constexpr int W_OFF = XS_OFF + MS * 4;           // weights [256 rows][4 chunks of 16 B]
-constexpr int WS_OFF = W_OFF + MN * MK / 2;      // weight scale words
-constexpr int STAGE = WS_OFF + MN * 4;           // 51200 B
-constexpr int P_OFF = NBUF * STAGE;              // route ids: two buffers of 256
+constexpr int W_OFF = MS * MK;                   // weights [256 rows][4 chunks of 16 B]
+constexpr int STAGE = W_OFF + MN * MK / 2;       // 48 KiB
+constexpr int SX_OFF = NBUF * STAGE;             // a scale group: activation scales [256 slots][16 B]
+constexpr int SW_OFF = SX_OFF + MS * 16;         // and weight scales [256 rows][16 B]
+constexpr int P_OFF = SW_OFF + MN * 16;          // route ids: two buffers of 256
 constexpr int B_OFF = P_OFF + 2 * 1024;          // bias: two buffers of 256 fp32
 constexpr int T_OFF = B_OFF + 2 * 1024;          // routing weights: two buffers of 256 fp32
-constexpr int LDS_BYTES = T_OFF + 2 * 1024;      // 156 KiB
+constexpr int LDS_BYTES = T_OFF + 2 * 1024;      // 158 KiB
 constexpr int GT = 4;                            // tiles sharing the weight blocks on one XCD
-constexpr int MIN_KT = 6;                        // stages per item the ring schedule needs
+constexpr int MIN_KT = 8;                        // stages per item the ring schedule needs
 
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the CU's LDS");
 
-// LDS-DMA loads a wavefront issues per stage: activations 8, their scales 1,
-// weights 4, their scales 1, the next tile's route ids 1, bias 1, routing
-// weights 1
+// LDS-DMA loads a wavefront issues for one stage: activations 8, weights 4,
+// the next item's route ids 1, its bias 1 (BIAS), this item's routing
+// weights 1 (TOPW); the first stage of a scale group also loads the
+// group's activation and weight scales (16 bytes a row: 4 stages)
 template <bool BIAS, bool TOPW>
-constexpr int dma_per_stage() { return 15 + (BIAS ? 1 : 0) + (TOPW ? 1 : 0); }
+constexpr int dma_base() { return 13 + (BIAS ? 1 : 0) + (TOPW ? 1 : 0); }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8); counters not named are not waited for
@@ -146,6 +148,10 @@ DEV int opaque(int v) {
   asm volatile("" : "+v"(v));
   return v;
 }
+DEV uint32_t ou(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // Word of slot s in a route-id buffer: the ids a lane's 8 activation loads
 // need are 8 consecutive words (wave w, lane group g = lane >> 3: slots
@@ -177,9 +183,11 @@ struct Item {
 };
 
 // Per-lane 32-bit source offsets of one item's loads (the stage's K offset
-// goes into the wave-uniform base).
+// goes into the wave-uniform base): activation and weight chunks, the scale
+// rows of this lane's scale-group load (slot / weight-row position
+// 64 wave + lane), its routing weight (TOPW).
 struct Src {
-  uint32_t x[8], xs, w[4], ws, tw;
+  uint32_t x[8], w[4], xs, ws, tw;
 };
 
 // Fragments of one 64-K half stage: weight tiles m (this lane's row, K half
@@ -188,8 +196,10 @@ struct Frag {
   u32x4_t w[4];
   u32x4_t x[4][2];
 };
-struct Scales {
-  u32x4_t w, x;  // scale words: weight tile m / slot tile n, 4 blocks of 32 K each
+// A scale group in registers: this lane's rows of weight tiles m and slot
+// tiles n, 16 E8M0 bytes each (word g: the 4 blocks of the group's stage g).
+struct Group {
+  u32x4_t w[4], x[4];
 };
 
 // A wave-uniform load through the scalar cache.  Through the constant
@@ -216,19 +226,20 @@ DEV Src sources(const MArgs& a, const Item& it, const uint8_t* P, int wave, int 
   const int lane = opaque(lane_);
   Src s;
   const int g = lane >> 3;
-  auto row_of = [&](int slot, int32_t route) -> int64_t {
-    if constexpr (GEMM == 1) return (int64_t)(route / a.top_k);
-    return (int64_t)it.pt * MS + min(slot, it.valid - 1);
+  // (32-bit arithmetic: the host checks that every offset fits in 31 bits)
+  const uint32_t rb = (uint32_t)a.a_row_bytes, sb = (uint32_t)a.a_sf_row;
+  auto row_of = [&](int slot, int32_t route) -> uint32_t {
+    if constexpr (GEMM == 1) return (uint32_t)(route / a.top_k);
+    return (uint32_t)(it.pt * MS + min(slot, it.valid - 1));
   };
+  const int p = 64 * wave + lane;  // slot / weight-row position of this lane's scale loads
   int32_t rt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int32_t first = 0, rts = 0;
-  const int p = 64 * wave + lane;
-  const int sslot = 128 * (p >> 7) + 32 * (p & 3) + ((p >> 2) & 31);  // slot of this lane's scale word
+  int32_t first = 0, rp = 0;
+  if constexpr (GEMM == 1 || TOPW) rp = *reinterpret_cast<const int32_t*>(P + 4 * p_word(p));
   if constexpr (GEMM == 1) {
     const u32x4_t r0 = *reinterpret_cast<const u32x4_t*>(P + 4 * (64 * wave + 8 * g));
     const u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(P + 4 * (64 * wave + 8 * g) + 16);
     first = *reinterpret_cast<const int32_t*>(P);
-    rts = *reinterpret_cast<const int32_t*>(P + 4 * p_word(sslot));
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       rt[j] = (int32_t)r0[j];
@@ -239,91 +250,47 @@ DEV Src sources(const MArgs& a, const Item& it, const uint8_t* P, int wave, int 
   for (int j = 0; j < 8; j++) {
     const int slot = 64 * wave + 8 * j + g;
     const int c = (lane & 7) ^ ((slot >> 1) & 7);  // logical chunk of physical chunk lane & 7
-    const int64_t row = row_of(slot, slot < it.valid ? rt[j] : first);
-    s.x[j] = (uint32_t)(row * a.a_row_bytes + 16 * c);
+    s.x[j] = row_of(slot, slot < it.valid ? rt[j] : first) * rb + 16u * c;
   }
-  s.xs = (uint32_t)(row_of(sslot, sslot < it.valid ? rts : first) * a.a_sf_row);
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int b = 64 * wave + 16 * j + (lane >> 2);
     const int c = (lane & 3) ^ ((b >> 2) & 3);
-    s.w[j] = (uint32_t)(weight_row<GEMM>(a, it.nb, b) * (a.K / 2) + 16 * c);
+    s.w[j] = (uint32_t)weight_row<GEMM>(a, it.nb, b) * (uint32_t)(a.K / 2) + 16u * c;
   }
-  s.ws = (uint32_t)(weight_row<GEMM>(a, it.nb, sslot) * (a.K / 32));
+  s.xs = row_of(p, p < it.valid ? rp : first) * sb;
+  s.ws = (uint32_t)weight_row<GEMM>(a, it.nb, p) * (uint32_t)(a.K / 32);
   // routing weight of slot p (padding slots load entry 0; it is not used)
-  s.tw = 0;
-  if constexpr (TOPW) s.tw = 4u * (uint32_t)max(0, *reinterpret_cast<const int32_t*>(P + 4 * p_word(p)));
+  s.tw = TOPW ? 4u * (uint32_t)max(0, rp) : 0u;
   return s;
 }
 
-// Where a stage's loads go and what the per-item extras are.
+// What one stage loads, and where to.
 struct Dst {
-  const uint8_t *xb, *xsb, *wb, *wsb;  // the stage's sources: activations, their scales, weights, theirs
-  uint8_t* st;              // stage buffer
-  const int32_t* p2e_tile;  // next tile's route ids -> P
+  const uint8_t *xb, *wb, *xsb, *wsb;  // sources at the stage's K offset: activations, weights, their scales
+  uint8_t* st;                         // stage buffer
+  const int32_t* p2e_tile;             // next item's route ids -> P
   uint8_t* P;
-  const float* bias;        // next item's 256 bias values (BIAS) -> B
+  const float* bias;                   // next item's 256 bias values (BIAS) -> B
   uint8_t* B;
-  uint8_t* T;               // routing weights of the sources' item (TOPW)
+  uint8_t* T;                          // routing weights of the sources' item (TOPW)
 };
 
-// Sources of the stage at K offset k0 of item it.
 DEV void stage_bases(const MArgs& a, const Item& it, int k0, Dst& d) {
   const int64_t wrow0 = (int64_t)it.e * a.rows_per_expert;
   d.xb = a.A + k0;
-  d.xsb = a.A_sf + k0 / 32;
   d.wb = a.W + wrow0 * (a.K / 2) + k0 / 2;
+  d.xsb = a.A_sf + k0 / 32;
   d.wsb = a.W_sf + wrow0 * (a.K / 32) + k0 / 32;
 }
 
-template <bool BIAS, bool TOPW>
-DEV void issue(const MArgs& a, const Dst& d, const Src& s, uint32_t p_lane, uint32_t b_lane, int wave) {
-  const uint8_t *xb = d.xb, *xsb = d.xsb, *wb = d.wb, *wsb = d.wsb;
-#pragma unroll
-  for (int j = 0; j < 8; j++) dma16(xb + s.x[j], d.st + X_OFF + 1024 * (8 * wave + j));
-  dma4(xsb + s.xs, d.st + XS_OFF + 256 * wave);
-#pragma unroll
-  for (int j = 0; j < 4; j++) dma16(wb + s.w[j], d.st + W_OFF + 1024 * (4 * wave + j));
-  dma4(wsb + s.ws, d.st + WS_OFF + 256 * wave);
-  dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + p_lane, d.P + 256 * wave);
-  if constexpr (BIAS) dma4(reinterpret_cast<const uint8_t*>(d.bias) + b_lane, d.B + 256 * wave);
-  if constexpr (TOPW) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + s.tw, d.T + 256 * wave);
-}
-
-DEV void read_frag(const uint8_t* st, int wo, int xa, int xb, Frag& f) {
-#pragma unroll
-  for (int m = 0; m < 4; m++) f.w[m] = *reinterpret_cast<const u32x4_t*>(st + wo + 2048 * m);
-#pragma unroll
-  for (int n = 0; n < 4; n++) {
-    f.x[n][0] = *reinterpret_cast<const u32x4_t*>(st + xa + 4096 * n);
-    f.x[n][1] = *reinterpret_cast<const u32x4_t*>(st + xb + 4096 * n);
-  }
-}
-
-DEV void mfma_half(f32x16_t (&acc)[4][4], const Frag& f, const Scales& sc, int sh) {
-  int ws[4], xs[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    ws[i] = (int)((sc.w[i] >> sh) & 255u);
-    xs[i] = (int)((sc.x[i] >> sh) & 255u);
-  }
-#pragma unroll
-  for (int m = 0; m < 4; m++) {
-    const i32x8_t av = {(int)f.w[m][0], (int)f.w[m][1], (int)f.w[m][2], (int)f.w[m][3], 0, 0, 0, 0};
-#pragma unroll
-    for (int n = 0; n < 4; n++) {
-      const i32x8_t bv = {(int)f.x[n][0][0], (int)f.x[n][0][1], (int)f.x[n][0][2], (int)f.x[n][0][3],
-                          (int)f.x[n][1][0], (int)f.x[n][1][1], (int)f.x[n][1][2], (int)f.x[n][1][3]};
-      acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[m][n], 4, 0, 0, ws[m], 0, xs[n]);
-    }
-  }
-}
-
-// Per-lane LDS offsets of the fragment reads (swizzled chunks, see
-// sources) and of the per-item loads; recomputed for every item from an
-// opaque lane id, so that none of them is live across the epilogue.
+// Per-lane LDS offsets of the fragment and scale reads (swizzled chunks,
+// see sources) and of the per-item loads; recomputed for every item from
+// an opaque lane id, so that none of them is live across the epilogue.
 struct LaneOffs {
-  int wo0, wo1, xo0, xo1, xo2, xo3, wso, xso, sh0, sh1;
+  int wo0, wo1, xo0, xo1, xo2, xo3;  // fragment reads
+  int sw, sx;                        // scale records of weight tile 0 / slot tile 0 (+ 512 B a tile)
+  int sh;                            // 8 h: the byte of block 2 u + h in a stage's word is 2 u + h
   uint32_t p_lane, b_lane;
 };
 
@@ -341,10 +308,9 @@ DEV LaneOffs lane_offsets(const MArgs& a, int wave, int lane_) {
   L.xo1 = xrow + 16 * ((2 + h) ^ xsw);
   L.xo2 = xrow + 16 * ((4 + h) ^ xsw);
   L.xo3 = xrow + 16 * ((6 + h) ^ xsw);
-  L.wso = WS_OFF + (32 * ww + r) * 16;
-  L.xso = XS_OFF + (32 * ws + r) * 16;
-  L.sh0 = 8 * h;  // scale byte of block 2 u + h
-  L.sh1 = 16 + 8 * h;
+  L.sw = SW_OFF + 16 * (128 * ww + r);
+  L.sx = SX_OFF + 16 * (128 * ws + r);
+  L.sh = 8 * h;
   // route-id load: position 64 wave + lane holds slot 64 wave + 8 (lane & 7)
   // + (lane >> 3); bias load: value 64 wave + lane (GEMM1: gate columns
   // 0..127 of the block, then the up half)
@@ -354,54 +320,63 @@ DEV LaneOffs lane_offsets(const MArgs& a, int wave, int lane_) {
   return L;
 }
 
-// Second half of a stage, written in issue order: load i of the stage,
-// MFMA i on the second-half fragments f1, read i of the next stage's first
-// half into f0 / scn (READS; an item's last stage leaves them to after the
-// epilogue, which then has their registers).  (LDS-DMA loads are scheduling boundaries, so the
-// interleave is set here rather than left to the scheduler.)
-template <int NDMA, bool BIAS, bool TOPW, bool READS>
-DEV void second_half(const MArgs& a, f32x16_t (&acc)[4][4], const Frag& f1, const Scales& sc, const Dst& d,
-                     const Src& s, const LaneOffs& L, int wave, const uint8_t* stn, Frag& f0, Scales& scn) {
-  const uint8_t *xb = d.xb, *xsb = d.xsb, *wb = d.wb, *wsb = d.wsb;
-  int wsc[4], xsc[4];
+// The loads of one stage (the prologue's; the loop interleaves its own).
+template <bool BIAS, bool TOPW>
+DEV void issue(const MArgs& a, const Dst& d, const Src& s, const LaneOffs& L, uint8_t* smem, int wave, bool group) {
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    wsc[i] = (int)((sc.w[i] >> L.sh1) & 255u);
-    xsc[i] = (int)((sc.x[i] >> L.sh1) & 255u);
-  }
+  for (int j = 0; j < 8; j++) dma16(d.xb + ou(s.x[j]), d.st + X_OFF + 1024 * (8 * wave + j));
 #pragma unroll
-  for (int i = 0; i < 17; i++) {
-    if (i < NDMA) {
-      if (i < 8) dma16(xb + s.x[i], d.st + X_OFF + 1024 * (8 * wave + i));
-      else if (i == 8) dma4(xsb + s.xs, d.st + XS_OFF + 256 * wave);
-      else if (i < 13) dma16(wb + s.w[i - 9], d.st + W_OFF + 1024 * (4 * wave + i - 9));
-      else if (i == 13) dma4(wsb + s.ws, d.st + WS_OFF + 256 * wave);
-      else if (i == 14) dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + L.p_lane, d.P + 256 * wave);
-      else if (i == 15 && BIAS) dma4(reinterpret_cast<const uint8_t*>(d.bias) + L.b_lane, d.B + 256 * wave);
-      else if (TOPW) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + s.tw, d.T + 256 * wave);
-    }
-    if (i < 16) {
-      const int m = i >> 2, n = i & 3;
-      const i32x8_t av = {(int)f1.w[m][0], (int)f1.w[m][1], (int)f1.w[m][2], (int)f1.w[m][3], 0, 0, 0, 0};
-      const i32x8_t bv = {(int)f1.x[n][0][0], (int)f1.x[n][0][1], (int)f1.x[n][0][2], (int)f1.x[n][0][3],
-                          (int)f1.x[n][1][0], (int)f1.x[n][1][1], (int)f1.x[n][1][2], (int)f1.x[n][1][3]};
-      acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[m][n], 4, 0, 0, wsc[m], 0, xsc[n]);
-    }
-    if (!READS) continue;
-    if (i == 0) scn.w = *reinterpret_cast<const u32x4_t*>(stn + L.wso);
-    else if (i == 1) scn.x = *reinterpret_cast<const u32x4_t*>(stn + L.xso);
-    else if (i < 6) f0.w[i - 2] = *reinterpret_cast<const u32x4_t*>(stn + L.wo0 + 2048 * (i - 2));
-    else if (i < 14) {
-      const int n = (i - 6) >> 1, piece = (i - 6) & 1;
-      f0.x[n][piece] = *reinterpret_cast<const u32x4_t*>(stn + (piece ? L.xo1 : L.xo0) + 4096 * n);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+  for (int j = 0; j < 4; j++) dma16(d.wb + ou(s.w[j]), d.st + W_OFF + 1024 * (4 * wave + j));
+  dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + ou(L.p_lane), d.P + 256 * wave);
+  if constexpr (BIAS) dma4(reinterpret_cast<const uint8_t*>(d.bias) + ou(L.b_lane), d.B + 256 * wave);
+  if constexpr (TOPW) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + ou(s.tw), d.T + 256 * wave);
+  if (group) {
+    dma16(d.xsb + ou(s.xs), smem + SX_OFF + 1024 * wave);
+    dma16(d.wsb + ou(s.ws), smem + SW_OFF + 1024 * wave);
   }
 }
 
-// Instruction order of a stage's first half for the scheduler (groups:
-// 0x008 MFMA, 0x100 LDS read): its 12 fragment reads between the first 12
-// MFMAs.
+DEV void read_frag(const uint8_t* st, int wo, int xa, int xb, Frag& f) {
+#pragma unroll
+  for (int m = 0; m < 4; m++) f.w[m] = *reinterpret_cast<const u32x4_t*>(st + wo + 2048 * m);
+#pragma unroll
+  for (int n = 0; n < 4; n++) {
+    f.x[n][0] = *reinterpret_cast<const u32x4_t*>(st + xa + 4096 * n);
+    f.x[n][1] = *reinterpret_cast<const u32x4_t*>(st + xb + 4096 * n);
+  }
+}
+
+DEV void read_group(const uint8_t* smem, const LaneOffs& L, Group& g) {
+#pragma unroll
+  for (int m = 0; m < 4; m++) g.w[m] = *reinterpret_cast<const u32x4_t*>(smem + L.sw + 512 * m);
+#pragma unroll
+  for (int n = 0; n < 4; n++) g.x[n] = *reinterpret_cast<const u32x4_t*>(smem + L.sx + 512 * n);
+}
+
+DEV void mfma_one(f32x16_t& acc, const u32x4_t& w, const u32x4_t (&x)[2], int wsc, int xsc) {
+  const i32x8_t av = {(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+  const i32x8_t bv = {(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3],
+                      (int)x[1][0], (int)x[1][1], (int)x[1][2], (int)x[1][3]};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 0, 0, wsc, 0, xsc);
+}
+
+// First half of stage G of a group (K half u = 0): 16 MFMAs on f0.
+template <int G>
+DEV void first_half(f32x16_t (&acc)[4][4], const Frag& f, const Group& sg, int sh) {
+  int ws[4], xs[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    ws[i] = (int)((sg.w[i][G] >> sh) & 255u);
+    xs[i] = (int)((sg.x[i][G] >> sh) & 255u);
+  }
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+#pragma unroll
+    for (int n = 0; n < 4; n++) mfma_one(acc[m][n], f.w[m], f.x[n], ws[m], xs[n]);
+}
+
+// Instruction order of a first half for the scheduler (groups: 0x008
+// MFMA, 0x100 LDS read): its 12 fragment reads between the first 12 MFMAs.
 DEV void order_first_half() {
 #pragma unroll
   for (int i = 0; i < 12; i++) {
@@ -409,6 +384,54 @@ DEV void order_first_half() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+// Second half of stage G (K half u = 1), written in issue order: load i of
+// the stage, MFMA i on f1, read i of the next stage's first half into f0
+// (in the order the next first half uses them) and, at the group's last
+// stage, of the next group's scales into sg (this half's scale bytes are
+// taken from it before the loop).  READS false: an item's last
+// stage leaves them to after the epilogue, which then has their registers.
+// (LDS-DMA loads are scheduling boundaries, so the interleave is set here
+// rather than left to the scheduler.)
+template <int G, int NB, bool BIAS, bool TOPW, bool READS>
+DEV void second_half(const MArgs& a, f32x16_t (&acc)[4][4], const Frag& f1, Group& sg, const Dst& d,
+                     const Src& s, const LaneOffs& L, uint8_t* smem, int wave, const uint8_t* stn, Frag& f0) {
+  constexpr bool GDMA = G == 1;  // this stage loads the next group's scales
+  constexpr int ND = NB + (GDMA ? 2 : 0);
+  constexpr int NR = READS ? 12 + (G == GS - 1 ? 8 : 0) : 0;
+  constexpr int X0 = BIAS ? 1 : 0, X1 = X0 + (TOPW ? 1 : 0);
+  int wsc[4], xsc[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    wsc[i] = (int)((sg.w[i][G] >> (L.sh + 16)) & 255u);
+    xsc[i] = (int)((sg.x[i][G] >> (L.sh + 16)) & 255u);
+  }
+#pragma unroll
+  for (int i = 0; i < 20; i++) {
+    if (i < ND) {
+      // (offsets through opaque(): a zero-extension hoisted out of the loop
+      // would hold each offset in two registers and lose the scalar-base form)
+      if (i < 8) dma16(d.xb + ou(s.x[i]), d.st + X_OFF + 1024 * (8 * wave + i));
+      else if (i < 12) dma16(d.wb + ou(s.w[i - 8]), d.st + W_OFF + 1024 * (4 * wave + i - 8));
+      else if (i == 12) dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + ou(L.p_lane), d.P + 256 * wave);
+      else if (BIAS && i - 13 == 0) dma4(reinterpret_cast<const uint8_t*>(d.bias) + ou(L.b_lane), d.B + 256 * wave);
+      else if (TOPW && i - 13 == X0) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + ou(s.tw), d.T + 256 * wave);
+      else if (GDMA && i - 13 == X1) dma16(d.xsb + ou(s.xs), smem + SX_OFF + 1024 * wave);
+      else if (GDMA && i - 13 == X1 + 1) dma16(d.wsb + ou(s.ws), smem + SW_OFF + 1024 * wave);
+    }
+    if (i < 16) mfma_one(acc[i >> 2][i & 3], f1.w[i >> 2], f1.x[i & 3], wsc[i >> 2], xsc[i & 3]);
+    if (i < NR) {
+      if (i == 0) f0.w[0] = *reinterpret_cast<const u32x4_t*>(stn + L.wo0);
+      else if (i < 9) {
+        const int n = (i - 1) >> 1, piece = (i - 1) & 1;
+        f0.x[n][piece] = *reinterpret_cast<const u32x4_t*>(stn + (piece ? L.xo1 : L.xo0) + 4096 * n);
+      } else if (i < 12) f0.w[i - 8] = *reinterpret_cast<const u32x4_t*>(stn + L.wo0 + 2048 * (i - 8));
+      else if (i < 16) sg.w[i - 12] = *reinterpret_cast<const u32x4_t*>(smem + L.sw + 512 * (i - 12));
+      else sg.x[i - 16] = *reinterpret_cast<const u32x4_t*>(smem + L.sx + 512 * (i - 16));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // SwiGLU of one gate/up pair with the hardware exp2 and reciprocal (a few
@@ -575,7 +598,7 @@ template <int GEMM, bool ATOMIC, int AK, bool BIAS>
 __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr bool TOPW = GEMM == 2 && ATOMIC;
-  constexpr int NDMA = dma_per_stage<BIAS, TOPW>();
+  constexpr int NB = dma_base<BIAS, TOPW>();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ww = wave & 1, ws = wave >> 1;
@@ -628,19 +651,15 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
   int pb = 0;
 
   // route ids (and bias) of the first item, then its sources
-  {
-    const LaneOffs L0 = lane_offsets<GEMM>(a, wave, lane);
-    dma4(reinterpret_cast<const uint8_t*>(a.p2e + (int64_t)cur.pt * MS) + L0.p_lane, Pb(0) + 256 * wave);
-    if constexpr (BIAS) dma4(reinterpret_cast<const uint8_t*>(bias_of(cur)) + L0.b_lane, Bb(0) + 256 * wave);
-  }
+  LaneOffs L = lane_offsets<GEMM>(a, wave, lane);
+  dma4(reinterpret_cast<const uint8_t*>(a.p2e + (int64_t)cur.pt * MS) + ou(L.p_lane), Pb(0) + 256 * wave);
+  if constexpr (BIAS) dma4(reinterpret_cast<const uint8_t*>(bias_of(cur)) + ou(L.b_lane), Bb(0) + 256 * wave);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   ring_barrier();
   Src cs = sources<GEMM, TOPW>(a, cur, Pb(0), wave, lane);
 
-  LaneOffs L = lane_offsets<GEMM>(a, wave, lane);
-
-  // the first three stages; every stage's loads also refresh the next
-  // item's route ids and bias
+  // the first three stages (the first with its scale group); every stage's
+  // loads also refresh the next item's route ids and bias
   {
     Dst d;
     d.p2e_tile = a.p2e + (int64_t)nxt.pt * MS;
@@ -652,24 +671,23 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
     for (int s = 0; s < NBUF; s++) {
       d.st = smem + s * STAGE;
       stage_bases(a, cur, s * MK, d);
-      issue<BIAS, TOPW>(a, d, cs, L.p_lane, L.b_lane, wave);
+      issue<BIAS, TOPW>(a, d, cs, L, smem, wave, s == 0);
     }
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NB));
   ring_barrier();
 
   Frag f0, f1;
-  Scales sc, scn;
-
+  Group sg;
   f32x16_t acc[4][4];
   int buf = 0;
 #pragma unroll 1
   for (;;) {
-    // the first half of the item's first stage (visible since the last
-    // stage's barrier; its buffer is refilled only after the next barrier)
+    // the item's first scale group and the first half of its first stage
+    // (visible since the last stage's barrier; their buffers are refilled
+    // only after the next barrier)
     L = lane_offsets<GEMM>(a, wave, lane);
-    sc.w = *reinterpret_cast<const u32x4_t*>(smem + buf * STAGE + L.wso);
-    sc.x = *reinterpret_cast<const u32x4_t*>(smem + buf * STAGE + L.xso);
+    read_group(smem, L, sg);
     read_frag(smem + buf * STAGE, L.wo0, L.xo0, L.xo1, f0);
 #pragma unroll
     for (int m = 0; m < 4; m++)
@@ -678,47 +696,69 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; i++) acc[m][n][i] = 0.0f;
 
-    auto stage = [&](int s, auto last_) {
-      constexpr bool last = decltype(last_)::value;
-      const bool same = s + 3 < KT;
-      const int k0 = (same ? s + 3 : s + 3 - KT) * MK;
+    // stage s (G = s % GS) of the item; it loads stage s + 3 of the
+    // stream: of this item while SAME, else the next item's
+    auto stage = [&](int s, auto G_, auto last_, auto same_) {
+      constexpr int Gs = decltype(G_)::value;
+      constexpr bool last = decltype(last_)::value, same = decltype(same_)::value;
       uint8_t* st = smem + buf * STAGE;
       const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
       const uint8_t* stn = smem + nbuf * STAGE;
-
       // what this stage loads (scalar work, done among the first half's MFMAs)
       Dst d;
-      stage_bases(a, same ? cur : nxt, k0, d);
+      stage_bases(a, same ? cur : nxt, (same ? s + 3 : s + 3 - KT) * MK, d);
       d.st = st;
       d.p2e_tile = a.p2e + (int64_t)nxt.pt * MS;
       d.P = Pb(pb ^ 1);
       d.bias = BIAS ? bias_of(nxt) : nullptr;
       d.B = Bb(pb ^ 1);
       d.T = Tb(same ? pb : pb ^ 1);
+
       // first half: its fragments are in f0; read the second half's
       read_frag(st, L.wo1, L.xo2, L.xo3, f1);
-      mfma_half(acc, f0, sc, L.sh0);
+      first_half<Gs>(acc, f0, sg, L.sh);
       order_first_half();
       __builtin_amdgcn_sched_barrier(0);
       // stage + 1 has landed once only the last stage's loads are in flight
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
+      // (those of stage + 2: NB, and the scale group when it starts one)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NB + (Gs == 2 ? 2 : 0)));
       ring_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // every wave is done with this stage's buffer: refill it three stages
       // on; second half, while the next stage's first half is read
-      second_half<NDMA, BIAS, TOPW, !last>(a, acc, f1, sc, d, cs, L, wave, stn, f0, scn);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!last) sc = scn;
+      second_half<Gs, NB, BIAS, TOPW, !last>(a, acc, f1, sg, d, cs, L, smem, wave, stn, f0);
       buf = nbuf;
     };
+    using G0 = std::integral_constant<int, 0>;
+    using G1 = std::integral_constant<int, 1>;
+    using G2 = std::integral_constant<int, 2>;
+    using G3 = std::integral_constant<int, 3>;
+    const std::false_type no;
+    const std::true_type yes;
 #pragma unroll 1
-    for (int s = 0; s < KT - 1; s++) {
-      // the next item's sources, once its route ids have landed (the
-      // third stage's wait covered the loads of the first)
-      if (s == KT - 3) cs = sources<GEMM, TOPW>(a, nxt, Pb(pb ^ 1), wave, lane);
-      stage(s, std::false_type{});
+    for (int q = 0; q < KT / GS - 1; q++) {
+      stage(GS * q, G0{}, no, yes);
+      stage(GS * q + 1, G1{}, no, yes);
+      stage(GS * q + 2, G2{}, no, yes);
+      stage(GS * q + 3, G3{}, no, yes);
     }
-    stage(KT - 1, std::true_type{});
+    // the last group: from its second stage on, the loads are the next
+    // item's, whose route ids have landed (its first loads went out with
+    // this item's first stage)
+    stage(KT - 4, G0{}, no, yes);
+    __builtin_amdgcn_sched_barrier(0);
+    cs = sources<GEMM, TOPW>(a, nxt, Pb(pb ^ 1), wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(KT - 3, G1{}, no, no);
+    stage(KT - 2, G2{}, no, no);
+    stage(KT - 1, G3{}, yes, no);
+    // the accumulators are complete here: an MFMA whose result only the
+    // epilogue's guarded stores use may not be sunk into them (that would
+    // keep its operands live across the epilogue)
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+#pragma unroll
+      for (int n = 0; n < 4; n++) asm volatile("" : "+a"(acc[m][n]));
 
     if constexpr (GEMM == 1) epilogue1<AK, BIAS>(a, acc, cur, Bb(pb), ww, ws, lane);
     else epilogue2<ATOMIC, BIAS>(a, acc, cur, Pb(pb), Bb(pb), Tb(pb), ww, ws, lane);
@@ -769,25 +809,25 @@ hipError_t launch_one(const MArgs& a, int max_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 constexpr int64_t OFF_LIMIT = (int64_t)1 << 31;  // the 32-bit lane offsets stay below this
 
 }  // namespace
 
-// 256-slot plan tiles; K a multiple of 128 with at least MIN_KT stages;
-// whole weight-row blocks; 16-byte aligned rows; 4-byte aligned scale rows
-// and arrays; every source offset inside 31 bits
+// 256-slot plan tiles; K a multiple of 512 (whole scale groups) with at
+// least MIN_KT stages; whole weight-row blocks; 16-byte aligned rows and
+// scale arrays; every source offset inside 31 bits
 bool mxw_supported1(const Gemm1Params& p) {
   const int64_t stride = p.x_row_stride ? p.x_row_stride : p.H;
   const int IP = gemm1_pairs(p);
-  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == MS && p.H % MK == 0 && p.H / MK >= MIN_KT &&
-         IP % 128 == 0 && stride % 16 == 0 && ((uintptr_t)p.x & 15) == 0 && aligned4(p.x_sf) &&
-         aligned4(p.w1_sf) && ((uintptr_t)p.y1 & 15) == 0 && ((uintptr_t)p.w1 & 15) == 0 &&
+  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == MS && p.H % (MK * GS) == 0 && p.H / MK >= MIN_KT &&
+         IP % 128 == 0 && stride % 16 == 0 && ((uintptr_t)p.x & 15) == 0 && aligned16(p.x_sf) &&
+         aligned16(p.w1_sf) && ((uintptr_t)p.y1 & 15) == 0 && ((uintptr_t)p.w1 & 15) == 0 &&
          (int64_t)p.plan->M * stride < OFF_LIMIT && (int64_t)2 * IP * (p.H / 2) < OFF_LIMIT;
 }
 bool mxw_supported2(const Gemm2Params& p) {
-  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == MS && p.I % MK == 0 && p.I / MK >= MIN_KT &&
-         p.H % MN == 0 && ((uintptr_t)p.y1 & 15) == 0 && aligned4(p.y1_sf) && aligned4(p.w2_sf) &&
+  return p.mode == MOE_QUANT_MXFP8_MXFP4 && p.plan->tile == MS && p.I % (MK * GS) == 0 && p.I / MK >= MIN_KT &&
+         p.H % MN == 0 && ((uintptr_t)p.y1 & 15) == 0 && aligned16(p.y1_sf) && aligned16(p.w2_sf) &&
          ((uintptr_t)p.w2 & 15) == 0 && (!p.y2 || ((uintptr_t)p.y2 & 15) == 0) &&
          p.plan->route_slots * p.I < OFF_LIMIT && (int64_t)p.H * (p.I / 2) < OFF_LIMIT;
 }

@@ -56,17 +56,17 @@ CASES = {
                                              activation=oracle.ACT_RELU2)),
     "mx_relu2_partial": (oracle.MXFP8_MXFP4, dict(M=300, H=192, I=320, E=8, El=6, k=3, seed=85, offset=1,
                                                   router_bias_std=0.7, activation=oracle.ACT_RELU2)),
-    # K of at least 768 in both GEMMs: with 256-slot tiles the MX mode takes the LDS-DMA ring kernels
+    # K of 1024 and more in both GEMMs: with 256-slot tiles the MX mode takes the LDS-DMA ring kernels
     # (the large-batch shape of pull request 4440's benchmark), here with ragged tiles, an expert
     # window and every FC1 activation
-    "mx_k768": (oracle.MXFP8_MXFP4, dict(M=300, H=768, I=768, E=8, El=6, k=3, seed=86, offset=1,
-                                         router_bias_std=0.7, swiglu_limit=2.0)),
-    "mx_k768_relu2": (oracle.MXFP8_MXFP4, dict(M=300, H=768, I=1024, E=8, El=6, k=3, seed=87, offset=1,
-                                               router_bias_std=0.7, activation=oracle.ACT_RELU2)),
-    "mx_k768_geglu": (oracle.MXFP8_MXFP4, dict(M=200, H=1024, I=768, E=8, El=8, k=3, seed=88,
-                                               activation=oracle.ACT_GEGLU_TANH)),
-    "mx_k768_situ": (oracle.MXFP8_MXFP4, dict(M=200, H=768, I=768, E=8, El=8, k=3, seed=89, situ_beta=0.1,
-                                              situ_linear_beta=0.08)),
+    "mx_k1024": (oracle.MXFP8_MXFP4, dict(M=300, H=1024, I=1024, E=8, El=6, k=3, seed=86, offset=1,
+                                          router_bias_std=0.7, swiglu_limit=2.0)),
+    "mx_k1024_relu2": (oracle.MXFP8_MXFP4, dict(M=300, H=1024, I=1024, E=8, El=6, k=3, seed=87, offset=1,
+                                                router_bias_std=0.7, activation=oracle.ACT_RELU2)),
+    "mx_k1536_geglu": (oracle.MXFP8_MXFP4, dict(M=200, H=1536, I=1024, E=8, El=8, k=3, seed=88,
+                                                activation=oracle.ACT_GEGLU_TANH)),
+    "mx_k1024_situ": (oracle.MXFP8_MXFP4, dict(M=200, H=1024, I=1536, E=8, El=8, k=3, seed=89, situ_beta=0.1,
+                                               situ_linear_beta=0.08)),
 }
 
 _cache = {}
@@ -183,7 +183,7 @@ def test_atomic_finalize_and_accumulate(name):
 
 
 SCALED = ["w4a16_basic", "w4a16_wide", "w4a16_stream", "w4a4_offset", "w4a4_tall", "mx_tall", "w4a16_partial",
-          "w4a4_partial", "mx_partial", "mx_k768"]
+          "w4a4_partial", "mx_partial", "mx_k1024"]
 
 
 def scaled_problem(name):
@@ -226,7 +226,7 @@ def test_scales_and_routed_scaling(name, tile):
     check_close(host(out, np.uint16), want, p.mode, f"{name} scaled atomic")
 
 
-@pytest.mark.parametrize("name", ["mx_k768", "mx_k768_relu2", "mx_k768_situ"])
+@pytest.mark.parametrize("name", ["mx_k1024", "mx_k1024_relu2", "mx_k1024_situ"])
 def test_mx_wide_tile_finalize(name):
     """256-slot tiles in the MX mode (the LDS-DMA ring kernels, whose GEMM2
     epilogue also does the atomic finalize): atomic finalize onto garbage,
@@ -262,7 +262,7 @@ def test_mx_wide_tile_many_items():
 
     import mixture_experts_forward_moe_amd as moe
     from gpu_util import DeviceProblem, check_close, host, say
-    wl = synth.small_workload(oracle.MXFP8_MXFP4, 4096, 2048, 768, 8, 8, 4, 90, router_bias_std=0.5)
+    wl = synth.small_workload(oracle.MXFP8_MXFP4, 4096, 2048, 1024, 8, 8, 4, 90, router_bias_std=0.5)
     p = oracle.quantize_problem(synth.make_raw(wl))
     say("MX 256-slot tiles, several items per workgroup")
     d = DeviceProblem(p)
