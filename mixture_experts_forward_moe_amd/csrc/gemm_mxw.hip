@@ -163,18 +163,22 @@ DEV int p_word(int s) { return (s >> 6) * 64 + (s & 7) * 8 + ((s >> 3) & 7); }
 // column 16 h + j.
 DEV int tile_col(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
-// Row, inside its expert, of weight-row position b (0..255) of block nb.
+// Row of weight-row position b (0..255) of an item, counted from the
+// item's first row (expert e, block nb: row block_row(nb) of the expert;
+// GEMM1's up rows are I further on).
 template <int GEMM>
-DEV int weight_row(const MArgs& a, int nb, int b) {
+DEV int weight_row(const MArgs& a, int b) {
   const int col = tile_col(b & 31);
   if constexpr (GEMM == 1) {
     const int m = (b >> 5) & 3;
-    const int c = nb * 128 + 64 * (b >> 7) + 32 * (m & 1) + col;
+    const int c = 64 * (b >> 7) + 32 * (m & 1) + col;
     return m < 2 ? c : a.I + c;
   } else {
-    return nb * MN + (b & ~31) + col;
+    return (b & ~31) + col;
   }
 }
+template <int GEMM>
+DEV int block_row(int nb) { return nb * (GEMM == 1 ? 128 : MN); }
 
 // A work item's wave-uniform facts: plan tile, weight-row block, local
 // expert, routes in the tile.
@@ -182,12 +186,17 @@ struct Item {
   int pt, nb, e, valid;
 };
 
-// Per-lane 32-bit source offsets of one item's loads (the stage's K offset
-// goes into the wave-uniform base): activation and weight chunks, the scale
-// rows of this lane's scale-group load (slot / weight-row position
-// 64 wave + lane), its routing weight (TOPW).
+// Per-lane 32-bit source offsets (the stage's K offset, and what is
+// uniform over an item, go into the wave-uniform bases): the activation
+// chunks and the scale row of this lane's scale-group load (slot position
+// 64 wave + lane), its routing weight (TOPW) -- per item in GEMM1, whose
+// rows are gathered tokens -- and the weight chunks and weight scale row,
+// the same for every item.
 struct Src {
-  uint32_t x[8], w[4], xs, ws, tw;
+  uint32_t x[8], xs, tw;
+};
+struct WSrc {
+  uint32_t w[4], ws;
 };
 
 // Fragments of one 64-K half stage: weight tiles m (this lane's row, K half
@@ -220,7 +229,10 @@ DEV Item load_item(const MArgs& a, int pt, int nb) {
   return it;
 }
 
-// Source offsets of an item; its route ids are in buffer P.
+// Source offsets of an item; its route ids are in buffer P.  GEMM2's
+// activation rows are the tile's own slots (padding slots read their own,
+// unused rows of y1: an output element depends only on its own slot), so
+// without TOPW its offsets are the same for every item.
 template <int GEMM, bool TOPW>
 DEV Src sources(const MArgs& a, const Item& it, const uint8_t* P, int wave, int lane_) {
   const int lane = opaque(lane_);
@@ -228,11 +240,7 @@ DEV Src sources(const MArgs& a, const Item& it, const uint8_t* P, int wave, int 
   const int g = lane >> 3;
   // (32-bit arithmetic: the host checks that every offset fits in 31 bits)
   const uint32_t rb = (uint32_t)a.a_row_bytes, sb = (uint32_t)a.a_sf_row;
-  auto row_of = [&](int slot, int32_t route) -> uint32_t {
-    if constexpr (GEMM == 1) return (uint32_t)(route / a.top_k);
-    return (uint32_t)(it.pt * MS + min(slot, it.valid - 1));
-  };
-  const int p = 64 * wave + lane;  // slot / weight-row position of this lane's scale loads
+  const int p = 64 * wave + lane;  // slot position of this lane's scale-group load
   int32_t rt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int32_t first = 0, rp = 0;
   if constexpr (GEMM == 1 || TOPW) rp = *reinterpret_cast<const int32_t*>(P + 4 * p_word(p));
@@ -246,22 +254,35 @@ DEV Src sources(const MArgs& a, const Item& it, const uint8_t* P, int wave, int 
       rt[4 + j] = (int32_t)r1[j];
     }
   }
+  // GEMM1: the token of the slot's route (padding slots: the tile's first
+  // route); GEMM2: the slot, counted from the tile's first
+  auto row_of = [&](int slot, int32_t route) -> uint32_t {
+    if constexpr (GEMM == 1) return (uint32_t)((slot < it.valid ? route : first) / a.top_k);
+    return (uint32_t)slot;
+  };
 #pragma unroll
   for (int j = 0; j < 8; j++) {
     const int slot = 64 * wave + 8 * j + g;
     const int c = (lane & 7) ^ ((slot >> 1) & 7);  // logical chunk of physical chunk lane & 7
-    s.x[j] = row_of(slot, slot < it.valid ? rt[j] : first) * rb + 16u * c;
+    s.x[j] = row_of(slot, rt[j]) * rb + 16u * c;
   }
+  s.xs = row_of(p, rp) * sb;
+  // routing weight of slot p (padding slots load entry 0; it is not used)
+  s.tw = TOPW ? 4u * (uint32_t)max(0, rp) : 0u;
+  return s;
+}
+
+template <int GEMM>
+DEV WSrc weight_sources(const MArgs& a, int wave, int lane_) {
+  const int lane = opaque(lane_);
+  WSrc s;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int b = 64 * wave + 16 * j + (lane >> 2);
     const int c = (lane & 3) ^ ((b >> 2) & 3);
-    s.w[j] = (uint32_t)weight_row<GEMM>(a, it.nb, b) * (uint32_t)(a.K / 2) + 16u * c;
+    s.w[j] = (uint32_t)weight_row<GEMM>(a, b) * (uint32_t)(a.K / 2) + 16u * c;
   }
-  s.xs = row_of(p, p < it.valid ? rp : first) * sb;
-  s.ws = (uint32_t)weight_row<GEMM>(a, it.nb, p) * (uint32_t)(a.K / 32);
-  // routing weight of slot p (padding slots load entry 0; it is not used)
-  s.tw = TOPW ? 4u * (uint32_t)max(0, rp) : 0u;
+  s.ws = (uint32_t)weight_row<GEMM>(a, 64 * wave + lane) * (uint32_t)(a.K / 32);
   return s;
 }
 
@@ -276,11 +297,13 @@ struct Dst {
   uint8_t* T;                          // routing weights of the sources' item (TOPW)
 };
 
+template <int GEMM>
 DEV void stage_bases(const MArgs& a, const Item& it, int k0, Dst& d) {
-  const int64_t wrow0 = (int64_t)it.e * a.rows_per_expert;
-  d.xb = a.A + k0;
+  const int64_t wrow0 = (int64_t)it.e * a.rows_per_expert + block_row<GEMM>(it.nb);
+  const int64_t xrow0 = GEMM == 1 ? 0 : (int64_t)it.pt * MS;  // GEMM2: the tile's first slot row
+  d.xb = a.A + xrow0 * a.a_row_bytes + k0;
   d.wb = a.W + wrow0 * (a.K / 2) + k0 / 2;
-  d.xsb = a.A_sf + k0 / 32;
+  d.xsb = a.A_sf + xrow0 * a.a_sf_row + k0 / 32;
   d.wsb = a.W_sf + wrow0 * (a.K / 32) + k0 / 32;
 }
 
@@ -322,17 +345,18 @@ DEV LaneOffs lane_offsets(const MArgs& a, int wave, int lane_) {
 
 // The loads of one stage (the prologue's; the loop interleaves its own).
 template <bool BIAS, bool TOPW>
-DEV void issue(const MArgs& a, const Dst& d, const Src& s, const LaneOffs& L, uint8_t* smem, int wave, bool group) {
+DEV void issue(const MArgs& a, const Dst& d, const Src& s, const WSrc& ws, const LaneOffs& L, uint8_t* smem, int wave,
+               bool group) {
 #pragma unroll
   for (int j = 0; j < 8; j++) dma16(d.xb + ou(s.x[j]), d.st + X_OFF + 1024 * (8 * wave + j));
 #pragma unroll
-  for (int j = 0; j < 4; j++) dma16(d.wb + ou(s.w[j]), d.st + W_OFF + 1024 * (4 * wave + j));
+  for (int j = 0; j < 4; j++) dma16(d.wb + ou(ws.w[j]), d.st + W_OFF + 1024 * (4 * wave + j));
   dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + ou(L.p_lane), d.P + 256 * wave);
   if constexpr (BIAS) dma4(reinterpret_cast<const uint8_t*>(d.bias) + ou(L.b_lane), d.B + 256 * wave);
   if constexpr (TOPW) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + ou(s.tw), d.T + 256 * wave);
   if (group) {
     dma16(d.xsb + ou(s.xs), smem + SX_OFF + 1024 * wave);
-    dma16(d.wsb + ou(s.ws), smem + SW_OFF + 1024 * wave);
+    dma16(d.wsb + ou(ws.ws), smem + SW_OFF + 1024 * wave);
   }
 }
 
@@ -396,7 +420,8 @@ DEV void order_first_half() {
 // rather than left to the scheduler.)
 template <int G, int NB, bool BIAS, bool TOPW, bool READS>
 DEV void second_half(const MArgs& a, f32x16_t (&acc)[4][4], const Frag& f1, Group& sg, const Dst& d,
-                     const Src& s, const LaneOffs& L, uint8_t* smem, int wave, const uint8_t* stn, Frag& f0) {
+                     const Src& s, const WSrc& ws, const LaneOffs& L, uint8_t* smem, int wave, const uint8_t* stn,
+                     Frag& f0) {
   constexpr bool GDMA = G == 1;  // this stage loads the next group's scales
   constexpr int ND = NB + (GDMA ? 2 : 0);
   constexpr int NR = READS ? 12 + (G == GS - 1 ? 8 : 0) : 0;
@@ -413,12 +438,12 @@ DEV void second_half(const MArgs& a, f32x16_t (&acc)[4][4], const Frag& f1, Grou
       // (offsets through opaque(): a zero-extension hoisted out of the loop
       // would hold each offset in two registers and lose the scalar-base form)
       if (i < 8) dma16(d.xb + ou(s.x[i]), d.st + X_OFF + 1024 * (8 * wave + i));
-      else if (i < 12) dma16(d.wb + ou(s.w[i - 8]), d.st + W_OFF + 1024 * (4 * wave + i - 8));
+      else if (i < 12) dma16(d.wb + ou(ws.w[i - 8]), d.st + W_OFF + 1024 * (4 * wave + i - 8));
       else if (i == 12) dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + ou(L.p_lane), d.P + 256 * wave);
       else if (BIAS && i - 13 == 0) dma4(reinterpret_cast<const uint8_t*>(d.bias) + ou(L.b_lane), d.B + 256 * wave);
       else if (TOPW && i - 13 == X0) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + ou(s.tw), d.T + 256 * wave);
       else if (GDMA && i - 13 == X1) dma16(d.xsb + ou(s.xs), smem + SX_OFF + 1024 * wave);
-      else if (GDMA && i - 13 == X1 + 1) dma16(d.wsb + ou(s.ws), smem + SW_OFF + 1024 * wave);
+      else if (GDMA && i - 13 == X1 + 1) dma16(d.wsb + ou(ws.ws), smem + SW_OFF + 1024 * wave);
     }
     if (i < 16) mfma_one(acc[i >> 2][i & 3], f1.w[i >> 2], f1.x[i & 3], wsc[i >> 2], xsc[i & 3]);
     if (i < NR) {
@@ -657,6 +682,7 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   ring_barrier();
   Src cs = sources<GEMM, TOPW>(a, cur, Pb(0), wave, lane);
+  WSrc wsrc = weight_sources<GEMM>(a, wave, lane);
 
   // the first three stages (the first with its scale group); every stage's
   // loads also refresh the next item's route ids and bias
@@ -670,8 +696,8 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
 #pragma unroll 1
     for (int s = 0; s < NBUF; s++) {
       d.st = smem + s * STAGE;
-      stage_bases(a, cur, s * MK, d);
-      issue<BIAS, TOPW>(a, d, cs, L, smem, wave, s == 0);
+      stage_bases<GEMM>(a, cur, s * MK, d);
+      issue<BIAS, TOPW>(a, d, cs, wsrc, L, smem, wave, s == 0);
     }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NB));
@@ -706,7 +732,7 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
       const uint8_t* stn = smem + nbuf * STAGE;
       // what this stage loads (scalar work, done among the first half's MFMAs)
       Dst d;
-      stage_bases(a, same ? cur : nxt, (same ? s + 3 : s + 3 - KT) * MK, d);
+      stage_bases<GEMM>(a, same ? cur : nxt, (same ? s + 3 : s + 3 - KT) * MK, d);
       d.st = st;
       d.p2e_tile = a.p2e + (int64_t)nxt.pt * MS;
       d.P = Pb(pb ^ 1);
@@ -726,7 +752,7 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       // every wave is done with this stage's buffer: refill it three stages
       // on; second half, while the next stage's first half is read
-      second_half<Gs, NB, BIAS, TOPW, !last>(a, acc, f1, sg, d, cs, L, smem, wave, stn, f0);
+      second_half<Gs, NB, BIAS, TOPW, !last>(a, acc, f1, sg, d, cs, wsrc, L, smem, wave, stn, f0);
       buf = nbuf;
     };
     using G0 = std::integral_constant<int, 0>;
@@ -746,9 +772,11 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
     // item's, whose route ids have landed (its first loads went out with
     // this item's first stage)
     stage(KT - 4, G0{}, no, yes);
-    __builtin_amdgcn_sched_barrier(0);
-    cs = sources<GEMM, TOPW>(a, nxt, Pb(pb ^ 1), wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (GEMM == 1 || TOPW) {
+      __builtin_amdgcn_sched_barrier(0);
+      cs = sources<GEMM, TOPW>(a, nxt, Pb(pb ^ 1), wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     stage(KT - 3, G1{}, no, no);
     stage(KT - 2, G2{}, no, no);
     stage(KT - 1, G3{}, yes, no);
