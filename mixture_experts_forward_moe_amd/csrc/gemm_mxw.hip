@@ -24,17 +24,20 @@
 //    the tile: a 32-column MXFP8 block of one y1 row is two lanes, its codes
 //    one 16-byte store per lane.
 //  - every operand goes global -> LDS with the LDS-DMA loads
-//    (global_load_lds: 16 bytes a lane, 4 for scale words and route ids)
-//    into a ring of 3 stages of 128 K; the ring runs on across work items,
-//    so the next item's first stages load while this item finishes and
-//    writes its epilogue.  A wavefront issues the same number of such loads
-//    every stage (activations 8, their scales 1, weights 4, their scales 1,
-//    the next item's route ids 1, and its bias and this item's routing
-//    weights when the epilogue uses them), so "stage s + 1 has landed" is a
-//    fixed vmcnt wait, then a bare s_barrier (a release fence would also
-//    wait for the loads in flight) publishes every wavefront's part.  The
-//    epilogue reads only LDS and scalars: a vector load there would make
-//    the compiler wait for every DMA in flight.
+//    (global_load_lds: 16 bytes a lane, 4 for route ids, bias and routing
+//    weights) into a ring of 3 stages of 128 K; the ring runs on across
+//    work items, so the next item's first stages load while this item
+//    finishes and writes its epilogue.  The E8M0 scales come in groups of 4
+//    stages (16 bytes a row) into one LDS area; each lane keeps its rows'
+//    records in registers.  A wavefront's loads per stage are fixed by the
+//    stage's place in its group (activations 8, weights 4; the next item's
+//    bias and this item's routing weights when the epilogue uses them; the
+//    group's scales and the next item's route ids with the group's first
+//    stage), so "stage s + 1 has landed" is a fixed vmcnt wait, then a bare
+//    s_barrier (a release fence would also wait for the loads in flight)
+//    publishes every wavefront's part.  The epilogue reads only LDS and
+//    scalars: a vector load there would make the compiler wait for every
+//    DMA in flight.
 //  - operand fragments are double-buffered in registers per 64-K half
 //    stage: the half-stage reads go out while the other half's 16 MFMAs
 //    run, so the matrix cores do not wait for LDS.  One barrier per stage.
@@ -83,11 +86,12 @@ constexpr int MIN_KT = 8;                        // stages per item the ring sch
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the CU's LDS");
 
 // LDS-DMA loads a wavefront issues for one stage: activations 8, weights 4,
-// the next item's route ids 1, its bias 1 (BIAS), this item's routing
-// weights 1 (TOPW); the first stage of a scale group also loads the
-// group's activation and weight scales (16 bytes a row: 4 stages)
+// the next item's bias 1 (BIAS), this item's routing weights 1 (TOPW); the
+// first stage of a scale group also loads the group's activation and
+// weight scales (16 bytes a row: 4 stages) and the next item's route ids
 template <bool BIAS, bool TOPW>
-constexpr int dma_base() { return 13 + (BIAS ? 1 : 0) + (TOPW ? 1 : 0); }
+constexpr int dma_base() { return 12 + (BIAS ? 1 : 0) + (TOPW ? 1 : 0); }
+constexpr int DMA_GROUP = 3;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8); counters not named are not waited for
@@ -351,10 +355,10 @@ DEV void issue(const MArgs& a, const Dst& d, const Src& s, const WSrc& ws, const
   for (int j = 0; j < 8; j++) dma16(d.xb + ou(s.x[j]), d.st + X_OFF + 1024 * (8 * wave + j));
 #pragma unroll
   for (int j = 0; j < 4; j++) dma16(d.wb + ou(ws.w[j]), d.st + W_OFF + 1024 * (4 * wave + j));
-  dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + ou(L.p_lane), d.P + 256 * wave);
   if constexpr (BIAS) dma4(reinterpret_cast<const uint8_t*>(d.bias) + ou(L.b_lane), d.B + 256 * wave);
   if constexpr (TOPW) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + ou(s.tw), d.T + 256 * wave);
   if (group) {
+    dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + ou(L.p_lane), d.P + 256 * wave);
     dma16(d.xsb + ou(s.xs), smem + SX_OFF + 1024 * wave);
     dma16(d.wsb + ou(ws.ws), smem + SW_OFF + 1024 * wave);
   }
@@ -422,8 +426,8 @@ template <int G, int NB, bool BIAS, bool TOPW, bool READS>
 DEV void second_half(const MArgs& a, f32x16_t (&acc)[4][4], const Frag& f1, Group& sg, const Dst& d,
                      const Src& s, const WSrc& ws, const LaneOffs& L, uint8_t* smem, int wave, const uint8_t* stn,
                      Frag& f0) {
-  constexpr bool GDMA = G == 1;  // this stage loads the next group's scales
-  constexpr int ND = NB + (GDMA ? 2 : 0);
+  constexpr bool GDMA = G == 1;  // this stage loads the next group's scales (and route ids)
+  constexpr int ND = NB + (GDMA ? DMA_GROUP : 0);
   constexpr int NR = READS ? 12 + (G == GS - 1 ? 8 : 0) : 0;
   constexpr int X0 = BIAS ? 1 : 0, X1 = X0 + (TOPW ? 1 : 0);
   int wsc[4], xsc[4];
@@ -439,11 +443,11 @@ DEV void second_half(const MArgs& a, f32x16_t (&acc)[4][4], const Frag& f1, Grou
       // would hold each offset in two registers and lose the scalar-base form)
       if (i < 8) dma16(d.xb + ou(s.x[i]), d.st + X_OFF + 1024 * (8 * wave + i));
       else if (i < 12) dma16(d.wb + ou(ws.w[i - 8]), d.st + W_OFF + 1024 * (4 * wave + i - 8));
-      else if (i == 12) dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + ou(L.p_lane), d.P + 256 * wave);
-      else if (BIAS && i - 13 == 0) dma4(reinterpret_cast<const uint8_t*>(d.bias) + ou(L.b_lane), d.B + 256 * wave);
-      else if (TOPW && i - 13 == X0) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + ou(s.tw), d.T + 256 * wave);
-      else if (GDMA && i - 13 == X1) dma16(d.xsb + ou(s.xs), smem + SX_OFF + 1024 * wave);
-      else if (GDMA && i - 13 == X1 + 1) dma16(d.wsb + ou(ws.ws), smem + SW_OFF + 1024 * wave);
+      else if (BIAS && i - 12 == 0) dma4(reinterpret_cast<const uint8_t*>(d.bias) + ou(L.b_lane), d.B + 256 * wave);
+      else if (TOPW && i - 12 == X0) dma4(reinterpret_cast<const uint8_t*>(a.topk_w) + ou(s.tw), d.T + 256 * wave);
+      else if (GDMA && i - 12 == X1) dma4(reinterpret_cast<const uint8_t*>(d.p2e_tile) + ou(L.p_lane), d.P + 256 * wave);
+      else if (GDMA && i - 12 == X1 + 1) dma16(d.xsb + ou(s.xs), smem + SX_OFF + 1024 * wave);
+      else if (GDMA && i - 12 == X1 + 2) dma16(d.wsb + ou(ws.ws), smem + SW_OFF + 1024 * wave);
     }
     if (i < 16) mfma_one(acc[i >> 2][i & 3], f1.w[i >> 2], f1.x[i & 3], wsc[i >> 2], xsc[i & 3]);
     if (i < NR) {
@@ -684,8 +688,8 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
   Src cs = sources<GEMM, TOPW>(a, cur, Pb(0), wave, lane);
   WSrc wsrc = weight_sources<GEMM>(a, wave, lane);
 
-  // the first three stages (the first with its scale group); every stage's
-  // loads also refresh the next item's route ids and bias
+  // the first three stages (the first with its scale group and the next
+  // item's route ids); every stage's loads also refresh the next item's bias
   {
     Dst d;
     d.p2e_tile = a.p2e + (int64_t)nxt.pt * MS;
@@ -746,8 +750,8 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
       order_first_half();
       __builtin_amdgcn_sched_barrier(0);
       // stage + 1 has landed once only the last stage's loads are in flight
-      // (those of stage + 2: NB, and the scale group when it starts one)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NB + (Gs == 2 ? 2 : 0)));
+      // (those of stage + 2: NB, and the group's when it starts one)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NB + (Gs == 2 ? DMA_GROUP : 0)));
       ring_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // every wave is done with this stage's buffer: refill it three stages
@@ -769,8 +773,8 @@ __global__ __launch_bounds__(MT, 1) void mxw_gemm_kernel(const MArgs a) {
       stage(GS * q + 3, G3{}, no, yes);
     }
     // the last group: from its second stage on, the loads are the next
-    // item's, whose route ids have landed (its first loads went out with
-    // this item's first stage)
+    // item's, whose route ids have landed (they went out with this item's
+    // second stage, and again with every group since)
     stage(KT - 4, G0{}, no, yes);
     if constexpr (GEMM == 1 || TOPW) {
       __builtin_amdgcn_sched_barrier(0);
