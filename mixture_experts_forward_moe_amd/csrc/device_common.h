@@ -17,6 +17,15 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 #define DEV __device__ __forceinline__
 
+// A wave-uniform load through the scalar cache.  Through the constant
+// address space, so the compiler does not fall back to a vector load (whose
+// wait would also wait for every other load in flight) when the kernel's
+// stores might alias; only for values the kernel does not write.
+template <typename T>
+DEV T ld_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)

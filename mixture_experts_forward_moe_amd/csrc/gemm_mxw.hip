@@ -215,15 +215,6 @@ struct Group {
   u32x4_t w[4], x[4];
 };
 
-// A wave-uniform load through the scalar cache.  Through the constant
-// address space, so the compiler does not fall back to a vector load (whose
-// wait would also wait for every DMA in flight) when the kernel's stores
-// might alias; none of the values read this way is written by the kernel.
-template <typename T>
-DEV T ld_uniform(const T* p) {
-  return *(const __attribute__((address_space(4))) T*)p;
-}
-
 DEV Item load_item(const MArgs& a, int pt, int nb) {
   Item it;
   it.pt = pt;
