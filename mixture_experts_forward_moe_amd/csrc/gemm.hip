@@ -532,6 +532,7 @@ static void plan_args(KArgs& a, const moe_plan_t* plan, int bm) {
 
 hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
   if (stream_supported(p.mode, p.plan, p.H, p.I)) return launch_gemm1_stream(p, stream);
+  if (nv_supported1(p)) return launch_gemm1_nv(p, stream);
   if (wide_supported1(p)) return launch_gemm1_wide(p, stream);
   if (mxw_supported1(p)) return launch_gemm1_mxw(p, stream);
   if (mx_supported1(p)) return launch_gemm1_mx(p, stream);
@@ -564,6 +565,7 @@ hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
 }
 
 hipError_t launch_gemm1_amax(const Gemm1Params& p, unsigned* amax, hipStream_t stream) {
+  if (nv_supported1(p)) return launch_gemm1_nv_amax(p, amax, stream);
   KArgs a = {};
   const int bm = pick_bm(p.plan->tile);
   plan_args(a, p.plan, bm);
@@ -592,6 +594,7 @@ hipError_t launch_gemm1_amax(const Gemm1Params& p, unsigned* amax, hipStream_t s
 
 hipError_t launch_gemm2(const Gemm2Params& p, hipStream_t stream) {
   if (!p.out && stream_supported(p.mode, p.plan, p.H, p.I)) return launch_gemm2_stream(p, 0, stream);
+  if (nv_supported2(p)) return launch_gemm2_nv(p, stream);
   if (wide_supported2(p)) return launch_gemm2_wide(p, stream);
   if (mxw_supported2(p)) return launch_gemm2_mxw(p, stream);
   if (mx_supported2(p)) return launch_gemm2_mx(p, stream);

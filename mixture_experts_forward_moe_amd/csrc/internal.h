@@ -79,6 +79,14 @@ bool mxw_supported2(const Gemm2Params& p);
 hipError_t launch_gemm1_mxw(const Gemm1Params& p, hipStream_t stream);
 hipError_t launch_gemm2_mxw(const Gemm2Params& p, hipStream_t stream);
 
+// NVFP4 x NVFP4 (W4A4) at plan tiles up to 64: one workgroup per (expert,
+// 256 weight rows) streams the weights once for all of the expert's routes
+bool nv_supported1(const Gemm1Params& p);
+bool nv_supported2(const Gemm2Params& p);
+hipError_t launch_gemm1_nv(const Gemm1Params& p, hipStream_t stream);
+hipError_t launch_gemm1_nv_amax(const Gemm1Params& p, unsigned* amax, hipStream_t stream);
+hipError_t launch_gemm2_nv(const Gemm2Params& p, hipStream_t stream);
+
 // weight-streaming kernels for 16-slot tiles (decode-sized batches)
 bool stream_supported(int mode, const moe_plan_t* plan, int H, int I);
 hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream);

@@ -67,6 +67,16 @@ CASES = {
                                                 activation=oracle.ACT_GEGLU_TANH)),
     "mx_k1024_situ": (oracle.MXFP8_MXFP4, dict(M=200, H=1024, I=1536, E=8, El=8, k=3, seed=89, situ_beta=0.1,
                                                situ_linear_beta=0.08)),
+    # NVFP4 x NVFP4 expert-streaming kernels (plan tiles up to 64, K a multiple of 256): experts
+    # with more routes than one 64-row pass, an odd number of K steps, partial weight-row blocks
+    # on either GEMM, and the other FC1 activations
+    "w4a4_stream": (oracle.W4A4, dict(M=300, H=1024, I=768, E=8, El=8, k=3, seed=91, router_bias_std=0.7)),
+    "w4a4_stream_n1": (oracle.W4A4, dict(M=100, H=512, I=320, E=6, El=5, k=2, seed=92, offset=1)),
+    "w4a4_stream_n2": (oracle.W4A4, dict(M=100, H=320, I=512, E=6, El=6, k=2, seed=93)),
+    "w4a4_stream_geglu": (oracle.W4A4, dict(M=64, H=512, I=512, E=8, El=8, k=2, seed=94,
+                                            activation=oracle.ACT_GEGLU_TANH)),
+    "w4a4_stream_relu2": (oracle.W4A4, dict(M=150, H=768, I=768, E=8, El=8, k=3, seed=95, router_bias_std=0.7,
+                                            activation=oracle.ACT_RELU2)),
 }
 
 _cache = {}
@@ -156,7 +166,7 @@ def test_forward(name, tile):
 
 
 @pytest.mark.parametrize("name", ["w4a16_basic", "w4a16_stream_offset", "w4a4_offset", "mx_offset", "mx_tall",
-                                  "w4a16_partial", "mx_partial"])
+                                  "w4a16_partial", "mx_partial", "w4a4_stream", "w4a4_stream_n2"])
 def test_atomic_finalize_and_accumulate(name):
     import torch
 
@@ -183,7 +193,7 @@ def test_atomic_finalize_and_accumulate(name):
 
 
 SCALED = ["w4a16_basic", "w4a16_wide", "w4a16_stream", "w4a4_offset", "w4a4_tall", "mx_tall", "w4a16_partial",
-          "w4a4_partial", "mx_partial", "mx_k1024"]
+          "w4a4_partial", "mx_partial", "mx_k1024", "w4a4_stream"]
 
 
 def scaled_problem(name):
