@@ -614,7 +614,7 @@ def main():
         line["prefill"] = secondary("prefill", wl2, r2, BF16_PEAK_TFLOPS, copy_gbs, "W4A16, bf16 MFMA")
         for name, key, peak, steps3, copies3, note in (
                 ("w4a4", "w4a4_nvfp4", BF16_PEAK_TFLOPS, 20, args.copies,
-                 "NVFP4 x and weights, bf16 MFMA after decode; fc2_input_scale calibrated on the device"),
+                 "NVFP4 x and weights, f16 MFMA after an exact decode of both; fc2_input_scale calibrated on the device"),
                 ("mx", "mxfp8_mxfp4_large", FP8_PEAK_TFLOPS, 6, 1,
                  "MXFP8 x, MXFP4 weights, scaled fp8 x fp4 MFMA (peak: dense fp8)")):
             wl3 = synth.WORKLOADS[key]
