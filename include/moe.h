@@ -83,6 +83,16 @@ typedef enum { MOE_FINALIZE_DETERMINISTIC = 0, MOE_FINALIZE_ATOMIC = 1 } moe_fin
  *          contiguous-window ordering of FlashInfer pull request 4440. */
 typedef enum { MOE_ROUTE_ORDER_AUTO = 0, MOE_ROUTE_ORDER_SINGLE = 1, MOE_ROUTE_ORDER_SPAN = 2 } moe_route_order_t;
 
+/* Which launch sequence moe_forward takes for a W4A16 batch at tile 16.
+ *  AUTO  : the two-launch decode path when it applies (see moe_forward) and
+ *          the batch is expected to give each local expert at most 1.25
+ *          routes (4 * M * top_k <= 5 * num_experts): it streams an expert's
+ *          weights once per route row, so beyond that the tiled path, which
+ *          streams them once per expert, is faster;
+ *  DECODE: the two-launch decode path whenever it applies;
+ *  TILED : never the decode path. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_TILED = 2 } moe_path_t;
+
 /* Routing plan (the moe_sort outputs of "vllm.models.flint.ops.moe_cute",
  * grouped_moe).  Route r = t * top_k + j.  Inside each local expert the
  * routes take consecutive slots in ascending r; each expert's range is
@@ -308,6 +318,7 @@ typedef struct moe_opts {
   const float* per_token_scale;  /* device fp32 [M], W4A4 only: GEMM1 input row scale; NULL = none */
   const float* fc1_bias;         /* device fp32 [E_l, 2I]: GEMM1 bias (moe_grouped_gemm1_act); NULL = none */
   const float* fc2_bias;         /* device fp32 [E_l, H]: GEMM2 bias (moe_grouped_gemm2_bias); NULL = none */
+  int path;                      /* moe_path_t, default AUTO */
 } moe_opts_t;
 
 #define MOE_NUM_PHASE_EVENTS 5
@@ -357,7 +368,8 @@ moe_status_t moe_forward_plan(moe_plan_t* plan, void* workspace, size_t workspac
  * output is zero-filled first by a kernel.  Decode-sized W4A16 batches
  * (tile 16, M * top_k <= 1024, H and I multiples of 512, I <= 8192,
  * 4-byte aligned w1_sf and w2_sf, and the routing plan plus one bf16 row
- * of H within 64 KiB of LDS) take two launches
+ * of H within 64 KiB of LDS; opts->path selects when, see moe_path_t) take
+ * two launches
  * instead: GEMM1 with the routing plan, then GEMM2 whose last workgroup per
  * 64 output columns applies the finalize; that finalize is the
  * deterministic one in either mode.

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 W4A16, W4A4, MXFP8_MXFP4 = 0, 1, 2
 FINALIZE_DETERMINISTIC, FINALIZE_ATOMIC = 0, 1
 ROUTE_ORDER_AUTO, ROUTE_ORDER_SINGLE, ROUTE_ORDER_SPAN = 0, 1, 2
+PATH_AUTO, PATH_DECODE, PATH_TILED = 0, 1, 2   # moe_path_t
 NUM_PHASE_EVENTS = 5
 FLT_MAX = 3.4028234663852886e38
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
@@ -54,7 +55,7 @@ class Opts(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t), ("phase_events", ctypes.c_void_p),
         ("activation", ctypes.c_int), ("situ_beta", ctypes.c_float), ("situ_linear_beta", ctypes.c_float),
         ("w1_alpha_up", ctypes.c_void_p), ("per_token_scale", ctypes.c_void_p),
-        ("fc1_bias", ctypes.c_void_p), ("fc2_bias", ctypes.c_void_p),
+        ("fc1_bias", ctypes.c_void_p), ("fc2_bias", ctypes.c_void_p), ("path", ctypes.c_int),
     ]
 
 
@@ -252,7 +253,7 @@ def make_opts(workspace=None, swiglu_alpha=1.0, swiglu_beta=0.0, swiglu_limit=FL
               routed_scaling_factor=1.0, accumulate=False, finalize_mode=FINALIZE_DETERMINISTIC,
               route_order=ROUTE_ORDER_AUTO, tile=0, x_row_stride=0, phase_events=None, activation=ACT_SWIGLU,
               situ_beta=0.0, situ_linear_beta=0.0, w1_alpha_up=None, per_token_scale=None, fc1_bias=None,
-              fc2_bias=None) -> Opts:
+              fc2_bias=None, path=PATH_AUTO) -> Opts:
     o = Opts()
     lib().moe_opts_init(ctypes.byref(o))
     o.swiglu_alpha, o.swiglu_beta, o.swiglu_limit = swiglu_alpha, swiglu_beta, swiglu_limit
@@ -268,6 +269,7 @@ def make_opts(workspace=None, swiglu_alpha=1.0, swiglu_beta=0.0, swiglu_limit=FL
     o.route_order = route_order
     o.tile = tile
     o.x_row_stride = x_row_stride
+    o.path = path
     if workspace is not None:
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["sort.hip", "gemm.hip", "gemm_wide.hip", "gemm_mx.hip", "gemm_mxw.hip", "gemm_nvfp4.hip", "stream.hip",
+SOURCES = ["sort.hip", "gemm.hip", "gemm_wide.hip", "gemm_mx.hip", "gemm_mxw.hip", "gemm_nvfp4.hip",
            "decode.hip", "finalize.hip", "capi.cpp", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -296,6 +296,7 @@ void moe_opts_init(moe_opts_t* o) {
   o->route_order = MOE_ROUTE_ORDER_AUTO;
   o->tile = 0;
   o->x_row_stride = 0;
+  o->path = MOE_PATH_AUTO;
 }
 
 int moe_default_tile(int M, int top_k, int num_experts, int num_local_experts, moe_quant_mode_t mode) {
@@ -359,6 +360,8 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   if (s != MOE_OK) return s;
   if (opts->finalize_mode != MOE_FINALIZE_DETERMINISTIC && opts->finalize_mode != MOE_FINALIZE_ATOMIC)
     return MOE_ERR_INVALID_ARGUMENT;
+  if (opts->path != MOE_PATH_AUTO && opts->path != MOE_PATH_DECODE && opts->path != MOE_PATH_TILED)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (M > 0 && (!x || !topk_ids || !topk_weights || !out)) return MOE_ERR_INVALID_ARGUMENT;
   if (!w1 || !w1_sf || !w1_alpha || !w2 || !w2_sf || !w2_alpha) return MOE_ERR_INVALID_ARGUMENT;
   if ((quant_mode == MOE_QUANT_W4A16) != (x_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
@@ -387,7 +390,12 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   uint8_t* y1_sf = (quant_mode == MOE_QUANT_W4A16) ? NULL : base;
   base += align256(y1_sf_bytes(quant_mode, L.slots, I));
   // (the decode kernels read scale pairs as aligned 32-bit words)
-  const bool dec = tile == 16 && decode_supported(quant_mode, M, top_k, num_local_experts, H, I) &&
+  // the decode path streams each expert's weights once per route row: by
+  // default it is taken only while the batch is expected to give a local
+  // expert at most 1.5 routes
+  const bool dec_wanted = opts->path == MOE_PATH_DECODE ||
+                          (opts->path == MOE_PATH_AUTO && 4 * (int64_t)M * top_k <= 5 * (int64_t)num_experts);
+  const bool dec = dec_wanted && tile == 16 && decode_supported(quant_mode, M, top_k, num_local_experts, H, I) &&
                    opts->x_row_stride % 8 == 0 && ((uintptr_t)w1_sf & 3) == 0 && ((uintptr_t)w2_sf & 3) == 0;
   uint16_t* y2 = (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC || dec) ? (uint16_t*)base : NULL;
 
@@ -439,10 +447,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
                (moe_route_order_t)opts->route_order, &plan, stream);
   if (s != MOE_OK) return s;
   if (mark(1) != hipSuccess) return MOE_ERR_DEVICE;
-  // small tiles: GEMM2 streams the weights and finalizes in route order in
-  // the same kernel (deterministic in either finalize mode)
-  const bool fused = stream_supported(quant_mode, &plan, H, I);
-  if (!fused && opts->finalize_mode == MOE_FINALIZE_ATOMIC && !opts->accumulate) {
+  if (opts->finalize_mode == MOE_FINALIZE_ATOMIC && !opts->accumulate) {
     if (launch_zero_fill(out, (size_t)M * H * 2, st) != hipSuccess) return MOE_ERR_DEVICE;
   }
   s = moe_grouped_gemm1_act(quant_mode, x, x_sf, opts->x_row_stride, &plan, w1, w1_sf, w1_alpha,
@@ -451,25 +456,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
                             opts->per_token_scale, opts->fc1_bias, y1, y1_sf, stream);
   if (s != MOE_OK) return s;
   if (mark(2) != hipSuccess) return MOE_ERR_DEVICE;
-  if (fused) {
-    Gemm2Params p = {};
-    p.mode = quant_mode;
-    p.y1 = y1;
-    p.y1_sf = y1_sf;
-    p.plan = &plan;
-    p.w2 = w2;
-    p.w2_sf = w2_sf;
-    p.w2_alpha = w2_alpha;
-    p.fc2_bias = opts->fc2_bias;
-    p.H = H;
-    p.I = I;
-    p.y2 = NULL;
-    p.topk_weights = topk_weights;
-    p.routed_scaling_factor = opts->routed_scaling_factor;
-    p.out = out;
-    if (launch_gemm2_stream(p, opts->accumulate, st) != hipSuccess) return MOE_ERR_DEVICE;
-    if (mark(3) != hipSuccess) return MOE_ERR_DEVICE;
-  } else if (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC) {
+  if (opts->finalize_mode == MOE_FINALIZE_DETERMINISTIC) {
     s = moe_grouped_gemm2_bias(quant_mode, y1, y1_sf, &plan, w2, w2_sf, w2_alpha, opts->fc2_bias, H, I, y2,
                                NULL, opts->routed_scaling_factor, NULL, stream);
     if (s != MOE_OK) return s;

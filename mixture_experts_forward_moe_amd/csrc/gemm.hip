@@ -531,7 +531,6 @@ static void plan_args(KArgs& a, const moe_plan_t* plan, int bm) {
 }
 
 hipError_t launch_gemm1(const Gemm1Params& p, hipStream_t stream) {
-  if (stream_supported(p.mode, p.plan, p.H, p.I)) return launch_gemm1_stream(p, stream);
   if (nv_supported1(p)) return launch_gemm1_nv(p, stream);
   if (wide_supported1(p)) return launch_gemm1_wide(p, stream);
   if (mxw_supported1(p)) return launch_gemm1_mxw(p, stream);
@@ -593,7 +592,6 @@ hipError_t launch_gemm1_amax(const Gemm1Params& p, unsigned* amax, hipStream_t s
 }
 
 hipError_t launch_gemm2(const Gemm2Params& p, hipStream_t stream) {
-  if (!p.out && stream_supported(p.mode, p.plan, p.H, p.I)) return launch_gemm2_stream(p, 0, stream);
   if (nv_supported2(p)) return launch_gemm2_nv(p, stream);
   if (wide_supported2(p)) return launch_gemm2_wide(p, stream);
   if (mxw_supported2(p)) return launch_gemm2_mxw(p, stream);

@@ -38,6 +38,8 @@
 //    items, so one expert's activation rows are read from one L2.
 // Requirements (else gemm.hip runs): K (H for GEMM1, I for GEMM2) a multiple
 // of 256; 16-byte aligned code arrays and row strides, 4-byte aligned scales.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -118,21 +120,42 @@ DEV int opaque(int v) {
   return v;
 }
 
+// E4M3 byte i (0..3, a constant after unrolling) of a dword as fp32
+DEV float e4m3_byte(uint32_t w, int i) {
+  switch (i) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+  }
+}
+
 // one K step of this lane's weights: 2 n-tiles x 64 codes + 4 scale bytes
 struct WStep {
   u32x4_t c[2][2];
   uint32_t s[2];
 };
-// one K step of this thread's activation part: 32 codes + 2 scale bytes
-struct AStep {
+// the two modes this file serves (the values of MOE_QUANT_W4A16 / MOE_QUANT_W4A4)
+enum { NV_W4A16 = 0, NV_W4A4 = 1 };
+
+// one K step of this thread's activation part.  W4A4: 32 codes + 2 scale
+// bytes of one row; W4A16: three 16-byte chunks of bf16 (rows of their own)
+template <int MODE> struct AStep;
+template <> struct AStep<NV_W4A4> {
   u32x4_t c;
   uint32_t s;
 };
+template <> struct AStep<NV_W4A16> {
+  u32x4_t c[3];
+};
+constexpr int NV_A16_CHUNKS = NV_RB * NV_KS * 2 / 16;  // 16-byte chunks of one bf16 step (1536)
 
 // AK: the FC1 activation (ACT_*), fixed per instantiation so that the
 // unrolled epilogue carries one kind's code
-template <int GEMM, bool ATOMIC, int AK>
+template <int MODE, int GEMM, bool ATOMIC, int AK>
 __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArgs a) {
+  // MFMA operands: f16 (W4A4, both sides decoded exactly) or bf16 (W4A16)
+  using op_t = std::conditional_t<MODE == NV_W4A4, f16x8_t, bf16x8_t>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[2 * NV_BUF];
   __shared__ int32_t row_src[NV_RB];
   __shared__ int32_t row_route[NV_RB];
@@ -201,26 +224,54 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
     }
     __syncthreads();
 
-    // threads past the pass's rows (and the 128 past NV_RB rows) load too:
-    // they read row 0 of A, which exists, and store nothing, so each step
-    // issues the same loads on every path
-    const bool a_ok = ar < valid;
-    const int asrc = a_ok ? row_src[ar] : 0;
-    const uint32_t aco = (uint32_t)asrc * (uint32_t)a.a_row_bytes + 16u * ap;
-    const uint32_t aso = (uint32_t)asrc * (uint32_t)a.a_sf_row + 2u * ap;
-    auto load_a = [&](AStep& b, int s) __attribute__((always_inline)) {
-      b.c = *reinterpret_cast<const u32x4_t*>(a.A + ou(aco + (uint32_t)s * (NV_KS / 2)));
-      b.s = *reinterpret_cast<const uint16_t*>(a.A_sf + ou(aso + (uint32_t)s * (NV_KS / 16)));
-    };
-    // decode into LDS step buffer `buf`: chunks 4 ap .. 4 ap + 3 of row ar
-    auto store_a = [&](const AStep& b, int buf) __attribute__((always_inline)) {
-      if (!a_ok) return;
-      const Sc4 sc = e4m3x4_f16(b.s);
-      uint8_t* row = xs + buf * NV_BUF + ar * NV_ROW + 64 * ap;
+    // Activation staging.  Threads past the pass's rows load too: they read
+    // row 0 of A, which exists, and store nothing, so each step issues the
+    // same loads on every path.
+    //  W4A4: thread (row ar, part ap) decodes K [32 ap, 32 ap + 32) of row ar;
+    //  W4A16: thread tid copies chunks tid, tid + 512, tid + 1024 of the
+    //  step (chunk c: row c / 32, K [8 (c % 32), + 8)).
+    bool a_ok[3];
+    uint32_t aco[3], aso = 0;
+    if constexpr (MODE == NV_W4A4) {
+      a_ok[0] = ar < valid;
+      const int asrc = a_ok[0] ? row_src[ar] : 0;
+      aco[0] = (uint32_t)asrc * (uint32_t)a.a_row_bytes + 16u * ap;
+      aso = (uint32_t)asrc * (uint32_t)a.a_sf_row + 2u * ap;
+    } else {
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const f16x8_t v = e2m1x8_f16(b.c[j], sc[j >> 1]);
-        *reinterpret_cast<f16x8_t*>(row + 16 * j) = v;
+      for (int i = 0; i < 3; i++) {
+        const int c = tid + NV_THREADS * i, row = c >> 5;
+        a_ok[i] = row < valid;
+        aco[i] = (uint32_t)(a_ok[i] ? row_src[row] : 0) * (uint32_t)a.a_row_bytes + 16u * (c & 31);
+      }
+    }
+    auto load_a = [&](AStep<MODE>& b, int s) __attribute__((always_inline)) {
+      if constexpr (MODE == NV_W4A4) {
+        b.c = *reinterpret_cast<const u32x4_t*>(a.A + ou(aco[0] + (uint32_t)s * (NV_KS / 2)));
+        b.s = *reinterpret_cast<const uint16_t*>(a.A_sf + ou(aso + (uint32_t)s * (NV_KS / 16)));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 3; i++)
+          b.c[i] = *reinterpret_cast<const u32x4_t*>(a.A + ou(aco[i] + (uint32_t)s * (NV_KS * 2)));
+      }
+    };
+    // into LDS step buffer `buf` (rows NV_ROW bytes apart, K in order)
+    auto store_a = [&](const AStep<MODE>& b, int buf) __attribute__((always_inline)) {
+      if constexpr (MODE == NV_W4A4) {
+        if (!a_ok[0]) return;
+        const Sc4 sc = e4m3x4_f16(b.s);
+        uint8_t* row = xs + buf * NV_BUF + ar * NV_ROW + 64 * ap;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const f16x8_t v = e2m1x8_f16(b.c[j], sc[j >> 1]);
+          *reinterpret_cast<f16x8_t*>(row + 16 * j) = v;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 3; i++) {
+          const int c = tid + NV_THREADS * i;
+          if (a_ok[i]) *reinterpret_cast<u32x4_t*>(xs + buf * NV_BUF + (c >> 5) * NV_ROW + 16 * (c & 31)) = b.c[i];
+        }
       }
     };
 
@@ -235,16 +286,32 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
 
       auto compute = [&](const WStep& w, int buf) __attribute__((always_inline)) {
         const uint8_t* xb = xs + buf * NV_BUF + r * NV_ROW + 128 * q;
-        const Sc4 sc0 = e4m3x4_f16(w.s[0]), sc1 = e4m3x4_f16(w.s[1]);
+        Sc4 sc0, sc1;
+        if constexpr (MODE == NV_W4A4) {
+          sc0 = e4m3x4_f16(w.s[0]);
+          sc1 = e4m3x4_f16(w.s[1]);
+        }
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-          const f16x8_t b0 = e2m1x8_f16(w.c[0][j >> 2][j & 3], sc0[j >> 1]);
-          const f16x8_t b1 = e2m1x8_f16(w.c[1][j >> 2][j & 3], sc1[j >> 1]);
+          op_t b0, b1;
+          if constexpr (MODE == NV_W4A4) {
+            b0 = e2m1x8_f16(w.c[0][j >> 2][j & 3], sc0[j >> 1]);
+            b1 = e2m1x8_f16(w.c[1][j >> 2][j & 3], sc1[j >> 1]);
+          } else {
+            // E2M1 x E4M3 is exact in bf16 as well (two instructions per element)
+            b0 = e2m1x8_scaled_to_bf16(w.c[0][j >> 2][j & 3], e4m3_byte(w.s[0], j >> 1));
+            b1 = e2m1x8_scaled_to_bf16(w.c[1][j >> 2][j & 3], e4m3_byte(w.s[1], j >> 1));
+          }
 #pragma unroll
           for (int m = 0; m < MT; m++) {
-            const f16x8_t af = *reinterpret_cast<const f16x8_t*>(xb + m * 16 * NV_ROW + 16 * j);
-            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b0, acc[m][0], 0, 0, 0);
-            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b1, acc[m][1], 0, 0, 0);
+            const op_t af = *reinterpret_cast<const op_t*>(xb + m * 16 * NV_ROW + 16 * j);
+            if constexpr (MODE == NV_W4A4) {
+              acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b0, acc[m][0], 0, 0, 0);
+              acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b1, acc[m][1], 0, 0, 0);
+            } else {
+              acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b0, acc[m][0], 0, 0, 0);
+              acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b1, acc[m][1], 0, 0, 0);
+            }
           }
           // one sub-step's operands live at a time
           __builtin_amdgcn_sched_barrier(0);
@@ -255,7 +322,7 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
       // flight while step s is consumed.  Loads past the last step re-read
       // the last one, so every step issues the same loads.
       WStep w0, w1, w2;
-      AStep an;
+      AStep<MODE> an;
       load_a(an, 0);
       load_w(w0, 0);
       load_w(w1, min(1, KT - 1));
@@ -320,6 +387,18 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
               mx = fmaxf(mx, fabsf(y[0][i]));
               if (two) mx = fmaxf(mx, fabsf(y[1][i]));
             }
+          }
+          if constexpr (MODE == NV_W4A16) {
+            uint16_t* Y = reinterpret_cast<uint16_t*>(a.Y);
+#pragma unroll
+            for (int h = 0; h < (two ? 2 : 1); h++)
+#pragma unroll
+              for (int i = 0; i < 4; i++) {
+                const int row = m * 16 + 4 * q + i;
+                if (row < valid && col_ok)
+                  Y[(int64_t)(slot_base + p0 + row) * a.n_out + col + h * a.IP] = f32_to_bf16(y[h][i]);
+              }
+            continue;
           }
           if (a.amax) continue;
           // NVFP4 with the global scale fc2_input_scale; a block is the 16
@@ -405,17 +484,22 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
 static bool al(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
 
 static bool nv_common(int mode, const moe_plan_t* plan, int K) {
-  return mode == MOE_QUANT_W4A4 && plan->tile <= 64 && K % NV_KS == 0 && K > 0;
+  return (mode == MOE_QUANT_W4A4 || mode == MOE_QUANT_W4A16) && plan->tile <= 64 && K % NV_KS == 0 && K > 0;
 }
 
 bool nv_supported1(const Gemm1Params& p) {
-  const int64_t stride = p.x_row_stride ? p.x_row_stride : p.H / 2;
-  return nv_common(p.mode, p.plan, p.H) && stride % 16 == 0 && al(p.x, 16) && al(p.x_sf, 4) && al(p.w1, 16) &&
-         al(p.w1_sf, 4) && gemm1_pairs(p) % 16 == 0;
+  if (!nv_common(p.mode, p.plan, p.H) || !al(p.w1, 16) || !al(p.w1_sf, 4) || gemm1_pairs(p) % 16 != 0) return false;
+  if (p.mode == MOE_QUANT_W4A4) {
+    const int64_t stride = p.x_row_stride ? p.x_row_stride : p.H / 2;
+    return stride % 16 == 0 && al(p.x, 16) && al(p.x_sf, 4);
+  }
+  const int64_t stride = p.x_row_stride ? p.x_row_stride : p.H;  // bf16 elements
+  return stride % 8 == 0 && al(p.x, 16);
 }
 
 bool nv_supported2(const Gemm2Params& p) {
-  return nv_common(p.mode, p.plan, p.I) && al(p.y1, 16) && al(p.y1_sf, 4) && al(p.w2, 16) && al(p.w2_sf, 4);
+  if (!nv_common(p.mode, p.plan, p.I) || !al(p.y1, 16) || !al(p.w2, 16) || !al(p.w2_sf, 4)) return false;
+  return p.mode == MOE_QUANT_W4A16 || al(p.y1_sf, 4);
 }
 
 static void nv_plan(NvArgs& a, const moe_plan_t* plan) {
@@ -426,21 +510,22 @@ static void nv_plan(NvArgs& a, const moe_plan_t* plan) {
   a.top_k = plan->top_k;
 }
 
-template <int GEMM, bool ATOMIC, int AK>
+template <int MODE, int GEMM, bool ATOMIC, int AK>
 static hipError_t nv_launch(const NvArgs& a, hipStream_t stream) {
   const int items = a.El * a.n_blocks;
   if (items == 0) return hipSuccess;
   const int grid = (items + 7) / 8 * 8;
-  nvfp4_stream_kernel<GEMM, ATOMIC, AK><<<grid, NV_THREADS, 0, stream>>>(a);
+  nvfp4_stream_kernel<MODE, GEMM, ATOMIC, AK><<<grid, NV_THREADS, 0, stream>>>(a);
   return hipGetLastError();
 }
 
+template <int MODE>
 static hipError_t nv_launch1(const NvArgs& a, hipStream_t stream) {
   switch (a.act.kind) {
-    case ACT_GEGLU_TANH: return nv_launch<1, false, ACT_GEGLU_TANH>(a, stream);
-    case ACT_SITU: return nv_launch<1, false, ACT_SITU>(a, stream);
-    case ACT_RELU2: return nv_launch<1, false, ACT_RELU2>(a, stream);
-    default: return nv_launch<1, false, ACT_SWIGLU>(a, stream);
+    case ACT_GEGLU_TANH: return nv_launch<MODE, 1, false, ACT_GEGLU_TANH>(a, stream);
+    case ACT_SITU: return nv_launch<MODE, 1, false, ACT_SITU>(a, stream);
+    case ACT_RELU2: return nv_launch<MODE, 1, false, ACT_RELU2>(a, stream);
+    default: return nv_launch<MODE, 1, false, ACT_SWIGLU>(a, stream);
   }
 }
 
@@ -449,8 +534,12 @@ static NvArgs nv_gemm1_args(const Gemm1Params& p) {
   nv_plan(a, p.plan);
   a.A = reinterpret_cast<const uint8_t*>(p.x);
   a.A_sf = p.x_sf;
-  a.a_row_bytes = p.x_row_stride ? p.x_row_stride : p.H / 2;
-  a.a_sf_row = p.H / 16;
+  if (p.mode == MOE_QUANT_W4A4) {
+    a.a_row_bytes = p.x_row_stride ? p.x_row_stride : p.H / 2;
+    a.a_sf_row = p.H / 16;
+  } else {
+    a.a_row_bytes = (p.x_row_stride ? p.x_row_stride : p.H) * 2;
+  }
   a.W = p.w1;
   a.W_sf = p.w1_sf;
   a.alpha = p.w1_alpha;
@@ -470,13 +559,14 @@ static NvArgs nv_gemm1_args(const Gemm1Params& p) {
 }
 
 hipError_t launch_gemm1_nv(const Gemm1Params& p, hipStream_t stream) {
-  return nv_launch1(nv_gemm1_args(p), stream);
+  if (p.mode == MOE_QUANT_W4A4) return nv_launch1<NV_W4A4>(nv_gemm1_args(p), stream);
+  return nv_launch1<NV_W4A16>(nv_gemm1_args(p), stream);
 }
 
 hipError_t launch_gemm1_nv_amax(const Gemm1Params& p, unsigned* amax, hipStream_t stream) {
   NvArgs a = nv_gemm1_args(p);
   a.amax = amax;
-  return nv_launch1(a, stream);
+  return nv_launch1<NV_W4A4>(a, stream);  // the calibration pass exists for W4A4 only
 }
 
 hipError_t launch_gemm2_nv(const Gemm2Params& p, hipStream_t stream) {
@@ -484,7 +574,7 @@ hipError_t launch_gemm2_nv(const Gemm2Params& p, hipStream_t stream) {
   nv_plan(a, p.plan);
   a.A = reinterpret_cast<const uint8_t*>(p.y1);
   a.A_sf = p.y1_sf;
-  a.a_row_bytes = p.I / 2;
+  a.a_row_bytes = p.mode == MOE_QUANT_W4A4 ? p.I / 2 : (int64_t)p.I * 2;
   a.a_sf_row = p.I / 16;
   a.W = p.w2;
   a.W_sf = p.w2_sf;
@@ -499,8 +589,12 @@ hipError_t launch_gemm2_nv(const Gemm2Params& p, hipStream_t stream) {
   a.topk_w = p.topk_weights;
   a.rsf = p.routed_scaling_factor;
   a.out = p.out;
-  if (p.out) return nv_launch<2, true, ACT_SWIGLU>(a, stream);
-  return nv_launch<2, false, ACT_SWIGLU>(a, stream);
+  if (p.mode == MOE_QUANT_W4A4) {
+    if (p.out) return nv_launch<NV_W4A4, 2, true, ACT_SWIGLU>(a, stream);
+    return nv_launch<NV_W4A4, 2, false, ACT_SWIGLU>(a, stream);
+  }
+  if (p.out) return nv_launch<NV_W4A16, 2, true, ACT_SWIGLU>(a, stream);
+  return nv_launch<NV_W4A16, 2, false, ACT_SWIGLU>(a, stream);
 }
 
 }  // namespace moe

@@ -87,12 +87,6 @@ hipError_t launch_gemm1_nv(const Gemm1Params& p, hipStream_t stream);
 hipError_t launch_gemm1_nv_amax(const Gemm1Params& p, unsigned* amax, hipStream_t stream);
 hipError_t launch_gemm2_nv(const Gemm2Params& p, hipStream_t stream);
 
-// weight-streaming kernels for 16-slot tiles (decode-sized batches)
-bool stream_supported(int mode, const moe_plan_t* plan, int H, int I);
-hipError_t launch_gemm1_stream(const Gemm1Params& p, hipStream_t stream);
-// y2 rows (p.y2) or, with p.out, the fused deterministic finalize into out
-hipError_t launch_gemm2_stream(const Gemm2Params& p, int accumulate, hipStream_t stream);
-
 // the two-launch W4A16 forward for decode-sized batches (plan tile 16)
 struct DecodeParams {
   const int32_t* topk_ids;

@@ -359,26 +359,28 @@ def test_decode_path_edge_cases(case):
     a single token, an expert window with a clamped SwiGLU."""
     import torch
 
+    import mixture_experts_forward_moe_amd as moe
+
     from gpu_util import DeviceProblem, check_close, dev, host, say
     say(f"decode edge case {case}")
     p = decode_case(case)
     assert takes_decode_path(p)
     d = DeviceProblem(p)
-    out = d.forward(tile=16)
+    out = d.forward(tile=16, path=moe.PATH_DECODE)
     torch.cuda.synchronize()
     want = oracle.forward_tokens(p, np.arange(p.M))
     if case == "no_local_routes":
         assert np.all(host(out, np.uint16) == 0) and np.all(want == 0)
         prev = synth.normal_bf16(3, 3, (p.M, p.H))
         out = dev(prev.copy())
-        d.forward(out=out, tile=16, accumulate=True)
+        d.forward(out=out, tile=16, path=moe.PATH_DECODE, accumulate=True)
         torch.cuda.synchronize()
         assert np.array_equal(host(out, np.uint16), prev)
     else:
         check_close(host(out, np.uint16), want, p.mode, f"decode {case}")
         prev = synth.normal_bf16(8, 8, (p.M, p.H), 0.0, 0.01)
         acc = dev(prev.copy())
-        d.forward(out=acc, tile=16, accumulate=True)
+        d.forward(out=acc, tile=16, path=moe.PATH_DECODE, accumulate=True)
         torch.cuda.synchronize()
         check_close(host(acc, np.uint16), oracle.forward_tokens(p, np.arange(p.M), accumulate=True, out_prev=prev),
                     p.mode, f"decode {case} accumulate")
@@ -397,6 +399,8 @@ def test_decode_forward_plan_bit_exact(case, fill):
     meeting the bar against the oracle."""
     import torch
 
+    import mixture_experts_forward_moe_amd as moe
+
     from gpu_util import DeviceProblem, assert_plan_equal, check_close, forward_in_workspace, host, say
     say(f"decode forward plan {case} fill {fill:#x}")
     if case == "w4a16_decode":
@@ -405,7 +409,7 @@ def test_decode_forward_plan_bit_exact(case, fill):
         p = decode_case(case)
     assert takes_decode_path(p)
     d = DeviceProblem(p)
-    out, plan = forward_in_workspace(d, 16, fill=fill)
+    out, plan = forward_in_workspace(d, 16, fill=fill, path=moe.PATH_DECODE)
     torch.cuda.synchronize()
     assert_plan_equal(plan, oracle.sort(p.topk_ids, p.num_local_experts, p.local_expert_offset, 16), case)
     want = oracle.forward_tokens(p, np.arange(p.M))
@@ -429,11 +433,11 @@ def test_decode_path_workspace_reuse():
     sizes = [moe.workspace_size(p.M, p.H, p.I, p.top_k, p.num_local_experts, 16, p.mode) for p in probs]
     ws = torch.full((max(sizes),), 0x7F, dtype=torch.uint8, device="cuda")
     devs = [DeviceProblem(p) for p in probs]
-    first = [d.forward(tile=16) for d in devs]  # fresh workspace each
+    first = [d.forward(tile=16, path=moe.PATH_DECODE) for d in devs]  # fresh workspace each
     torch.cuda.synchronize()
     for rep in range(3):
         for i in [0, 1, 3, 2, 0, 2, 1]:
-            out = devs[i].forward(tile=16, workspace=ws)
+            out = devs[i].forward(tile=16, path=moe.PATH_DECODE, workspace=ws)
             torch.cuda.synchronize()
             assert torch.equal(out, first[i]), (rep, i)
 
@@ -444,12 +448,14 @@ def test_decode_sized_batch_with_unaligned_scales():
     same results as aligned ones (deterministic finalize either way)."""
     import torch
 
+    import mixture_experts_forward_moe_amd as moe
+
     from gpu_util import DeviceProblem, check_close, host, say
     say("decode-sized batch, scale arrays at a 2-byte offset")
     p = decode_case("offset_swiglu")
     d = DeviceProblem(p)
     want = oracle.forward_tokens(p, np.arange(p.M))
-    aligned = d.forward(tile=16)
+    aligned = d.forward(tile=16, path=moe.PATH_DECODE)
     for name in ("w1_sf", "w2_sf"):
         t = getattr(d, name)
         base = torch.empty(t.numel() + 2, dtype=torch.uint8, device="cuda")
@@ -457,7 +463,7 @@ def test_decode_sized_batch_with_unaligned_scales():
         view.copy_(t)
         assert view.data_ptr() % 4 == 2
         setattr(d, name, view)
-    shifted = d.forward(tile=16)
+    shifted = d.forward(tile=16, path=moe.PATH_DECODE)
     torch.cuda.synchronize()
     check_close(host(shifted, np.uint16), want, p.mode, "unaligned scales")
     check_close(host(aligned, np.uint16), want, p.mode, "aligned scales")
@@ -478,18 +484,18 @@ def test_decode_path_graph_replay():
     d, e = DeviceProblem(p), DeviceProblem(q)
     n = max(moe.workspace_size(r.M, r.H, r.I, r.top_k, r.num_local_experts, 16, r.mode) for r in (p, q))
     ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
-    want = d.forward(tile=16, workspace=ws)
-    want_q = e.forward(tile=16, workspace=ws)
+    want = d.forward(tile=16, path=moe.PATH_DECODE, workspace=ws)
+    want_q = e.forward(tile=16, path=moe.PATH_DECODE, workspace=ws)
     torch.cuda.synchronize()
     out = torch.zeros_like(want)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        d.forward(out=out, tile=16, workspace=ws)
+        d.forward(out=out, tile=16, path=moe.PATH_DECODE, workspace=ws)
     for rep in range(4):
         out.zero_()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, want), rep
-        other = e.forward(tile=16, workspace=ws)  # eager work on the same workspace between replays
+        other = e.forward(tile=16, path=moe.PATH_DECODE, workspace=ws)  # eager work on the same workspace between replays
         torch.cuda.synchronize()
         assert torch.equal(other, want_q), rep
