@@ -187,8 +187,9 @@ moe_status_t moe_sort(const int32_t* topk_ids, int M, int top_k, int num_experts
  *                quantised with global scale *fc2_input_scale
  *   MXFP8_MXFP4: E4M3 [route_slots, I] + E8M0 y1_sf [route_slots, I/32]
  * Inputs (device): x as in moe_quant_mode_t with row stride x_row_stride in
- * x's storage units (bf16 elements, or bytes); x_sf contiguous, NULL in
- * W4A16.  w1 packed E2M1 [E_l, 2I, H/2]; w1_sf E4M3 [E_l, 2I, H/16] (NVFP4)
+ * x's storage units (bf16 elements, or bytes; 0 = contiguous rows; shorter
+ * than a row: MOE_ERR_INVALID_ARGUMENT; not a multiple of 16 bytes:
+ * MOE_ERR_UNSUPPORTED); x_sf contiguous, NULL in W4A16.  w1 packed E2M1 [E_l, 2I, H/2]; w1_sf E4M3 [E_l, 2I, H/16] (NVFP4)
  * or E8M0 [E_l, 2I, H/32] (MX); w1_alpha fp32 [E_l].  fc2_input_scale: a
  * device fp32 scalar, required in W4A4 and NULL otherwise.  H and I must be
  * multiples of the scale block (16 NVFP4, 32 MX; else

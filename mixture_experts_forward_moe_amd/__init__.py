@@ -17,6 +17,7 @@ W4A16, W4A4, MXFP8_MXFP4 = 0, 1, 2
 FINALIZE_DETERMINISTIC, FINALIZE_ATOMIC = 0, 1
 ROUTE_ORDER_AUTO, ROUTE_ORDER_SINGLE, ROUTE_ORDER_SPAN = 0, 1, 2
 PATH_AUTO, PATH_DECODE, PATH_TILED = 0, 1, 2   # moe_path_t
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE, ERR_SCRATCH_TOO_SMALL = range(6)  # moe_status_t
 NUM_PHASE_EVENTS = 5
 FLT_MAX = 3.4028234663852886e38
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES

@@ -151,6 +151,9 @@ def test_forward_argument_checks():
     o.finalize_mode = 3
     assert L.moe_forward(*args(0, None)) == INVALID
     o.finalize_mode = 0
+    o.path = 3
+    assert L.moe_forward(*args(0, None)) == INVALID
+    o.path = moe.PATH_AUTO
     assert L.moe_forward(F, None, F, F, F, F, F, F, F, F, 8, 2, 8, 0, 0, F, 16, 256, 512, None, None) == INVALID
 
 
@@ -210,6 +213,18 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     consts = dict(re.findall(r"#define\s+(MOE_\w+)\s+(\d+)", text))
     assert int(consts["MOE_NUM_PHASE_EVENTS"]) == moe.NUM_PHASE_EVENTS
+    enums = {k: int(v) for k, v in re.findall(r"\b(MOE_[A-Z0-9_]+)\s*=\s*(\d+)", text)}
+    binding = {"MOE_QUANT_W4A16": moe.W4A16, "MOE_QUANT_W4A4": moe.W4A4, "MOE_QUANT_MXFP8_MXFP4": moe.MXFP8_MXFP4,
+               "MOE_FINALIZE_DETERMINISTIC": moe.FINALIZE_DETERMINISTIC, "MOE_FINALIZE_ATOMIC": moe.FINALIZE_ATOMIC,
+               "MOE_ROUTE_ORDER_AUTO": moe.ROUTE_ORDER_AUTO, "MOE_ROUTE_ORDER_SINGLE": moe.ROUTE_ORDER_SINGLE,
+               "MOE_ROUTE_ORDER_SPAN": moe.ROUTE_ORDER_SPAN, "MOE_PATH_AUTO": moe.PATH_AUTO,
+               "MOE_PATH_DECODE": moe.PATH_DECODE, "MOE_PATH_TILED": moe.PATH_TILED,
+               "MOE_ACT_SWIGLU": moe.ACT_SWIGLU, "MOE_ACT_GEGLU_TANH": moe.ACT_GEGLU_TANH,
+               "MOE_ACT_RELU2": moe.ACT_RELU2, "MOE_OK": moe.OK, "MOE_ERR_INVALID_ARGUMENT": moe.ERR_INVALID_ARGUMENT,
+               "MOE_ERR_UNSUPPORTED": moe.ERR_UNSUPPORTED, "MOE_ERR_WORKSPACE": moe.ERR_WORKSPACE,
+               "MOE_ERR_DEVICE": moe.ERR_DEVICE, "MOE_ERR_SCRATCH_TOO_SMALL": moe.ERR_SCRATCH_TOO_SMALL}
+    for name, value in binding.items():
+        assert enums[name] == value, name
 
 
 def test_forward_plan_view():

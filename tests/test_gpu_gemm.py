@@ -77,6 +77,16 @@ CASES = {
                                             activation=oracle.ACT_GEGLU_TANH)),
     "w4a4_stream_relu2": (oracle.W4A4, dict(M=150, H=768, I=768, E=8, El=8, k=3, seed=95, router_bias_std=0.7,
                                             activation=oracle.ACT_RELU2)),
+    # the same kernels in W4A16 mode (bf16 activations copied, weights decoded to bf16)
+    "w4a16_stream_big": (oracle.W4A16, dict(M=300, H=1024, I=768, E=8, El=8, k=3, seed=96, router_bias_std=0.7)),
+    "w4a16_stream_n1": (oracle.W4A16, dict(M=100, H=512, I=320, E=6, El=5, k=2, seed=97, offset=1)),
+    "w4a16_stream_n2": (oracle.W4A16, dict(M=100, H=320, I=512, E=6, El=6, k=2, seed=98)),
+    "w4a16_stream_geglu": (oracle.W4A16, dict(M=64, H=512, I=512, E=8, El=8, k=2, seed=99,
+                                              activation=oracle.ACT_GEGLU_TANH)),
+    "w4a16_stream_situ": (oracle.W4A16, dict(M=80, H=768, I=512, E=8, El=7, k=3, seed=100, offset=1,
+                                             situ_beta=0.2, situ_linear_beta=0.05)),
+    "w4a16_stream_relu2": (oracle.W4A16, dict(M=150, H=768, I=768, E=8, El=8, k=3, seed=101, router_bias_std=0.7,
+                                              activation=oracle.ACT_RELU2)),
 }
 
 _cache = {}
@@ -166,7 +176,8 @@ def test_forward(name, tile):
 
 
 @pytest.mark.parametrize("name", ["w4a16_basic", "w4a16_stream_offset", "w4a4_offset", "mx_offset", "mx_tall",
-                                  "w4a16_partial", "mx_partial", "w4a4_stream", "w4a4_stream_n2"])
+                                  "w4a16_partial", "mx_partial", "w4a4_stream", "w4a4_stream_n2",
+                                  "w4a16_stream_big", "w4a16_stream_n1"])
 def test_atomic_finalize_and_accumulate(name):
     import torch
 
@@ -193,7 +204,7 @@ def test_atomic_finalize_and_accumulate(name):
 
 
 SCALED = ["w4a16_basic", "w4a16_wide", "w4a16_stream", "w4a4_offset", "w4a4_tall", "mx_tall", "w4a16_partial",
-          "w4a4_partial", "mx_partial", "mx_k1024", "w4a4_stream"]
+          "w4a4_partial", "mx_partial", "mx_k1024", "w4a4_stream", "w4a16_stream_big"]
 
 
 def scaled_problem(name):
@@ -290,17 +301,27 @@ def test_mx_wide_tile_many_items():
     check_close(host(out_a, np.uint16)[toks], want, p.mode, "many items atomic")
 
 
-def test_row_strided_x():
+@pytest.mark.parametrize("extra,tile", [(64, 0), (8, 32), (64, 128), (4, 32)])
+def test_row_strided_x(extra, tile):
+    """bf16 x rows `extra` elements apart beyond H (the expert-streaming
+    kernel at tile 32, the wide one at 128); a stride that is not a multiple
+    of 16 bytes is refused before anything runs"""
     import torch
 
+    import mixture_experts_forward_moe_amd as moe
     from gpu_util import DeviceProblem, check_close, host, say
     p = problem("w4a16_basic")
-    say("row-strided x")
+    say(f"row-strided x extra={extra} tile={tile}")
     d = DeviceProblem(p)
-    wide = torch.zeros((p.M, p.H + 64), dtype=torch.int16, device="cuda")
+    wide = torch.zeros((p.M, p.H + extra), dtype=torch.int16, device="cuda")
     wide[:, :p.H] = d.x
     d.x = wide
-    out = d.forward(x_row_stride=p.H + 64)
+    if extra % 8:
+        with pytest.raises(moe.MoeError) as e:
+            d.forward(x_row_stride=p.H + extra, tile=tile)
+        assert e.value.status == moe.ERR_UNSUPPORTED
+        return
+    out = d.forward(x_row_stride=p.H + extra, tile=tile)
     torch.cuda.synchronize()
     check_close(host(out, np.uint16), oracle.forward_tokens(p, np.arange(p.M)), p.mode, "strided")
 
