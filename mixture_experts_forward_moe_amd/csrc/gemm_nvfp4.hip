@@ -1,43 +1,50 @@
-// gemm_nvfp4.hip -- expert-streaming grouped GEMMs for NVFP4 x NVFP4 (W4A4)
-// at mid-sized batches: a few dozen routes per local expert, where GEMM1 and
+// gemm_nvfp4.hip -- expert-streaming grouped GEMMs on NVFP4 weights at
+// mid-sized batches (a few dozen routes per local expert), where GEMM1 and
 // GEMM2 are bound by HBM bandwidth on the weight bytes, not by the MFMAs.
+// Two modes, a template argument: NVFP4 activations (W4A4) and bf16
+// activations (W4A16).
 //
 // Same computation as gemm.hip ("flashinfer.fused_moe.cute_dsl_fused_moe",
-// Parameters: quant_mode w4a4, fc2_input_scale; "vllm.models.flint.ops.moe_cute",
+// Parameters: quant_mode, fc2_input_scale; "vllm.models.flint.ops.moe_cute",
 // module docstring):
 //   GEMM1: y1 = act(alpha1[e] * x W1[e]^T) for the routes of expert e, y1
-//          rounded once to bf16 and requantised to NVFP4 with fc2_input_scale;
+//          rounded once to bf16 (W4A4: then requantised to NVFP4 with
+//          fc2_input_scale);
 //   GEMM2: y2 = alpha2[e] * y1 W2[e]^T, stored as bf16 rows or weighted and
 //          added into out with packed-bf16 atomics.
 //
 // Organisation, for bandwidth:
 //  - a workgroup of 8 wavefronts owns one local expert, a block of 256
 //    weight rows (GEMM1: 128 gate rows and their 128 up rows; GEMM2: 256
-//    output columns) and the expert's routes, 48 at a time; with the usual
-//    one pass per expert, each weight byte leaves HBM once per forward and
-//    the tile padding of the plan costs nothing (the kernel walks
-//    expert_offsets / expert_counts).
+//    output columns) and the expert's routes, 48 (W4A4) or 32 (W4A16) at a
+//    time; with the usual one pass per expert, each weight byte leaves HBM
+//    once per forward and the tile padding of the plan costs nothing (the
+//    kernel walks expert_offsets / expert_counts).
 //  - each wavefront streams its 32 weight rows straight into registers, K
 //    256 at a time through a ring of three register steps (two steps of
 //    loads in flight while one is consumed), and decodes them right before
-//    the MFMA: one v_cvt_scalef32_pk_f16_fp4 turns two E2M1 codes into f16
-//    (its scale operand takes only a power of two) and one v_pk_mul_f16
-//    applies the E4M3 block scale.  An E2M1 value times an E4M3 value has at
-//    most 6 significant bits and lies in [2^-10, 2688], so the f16 operands
-//    are exact and v_mfma_f32_16x16x32_f16 (fp32 accumulation) forms the
-//    same products as a bf16 MFMA would.  128 VGPRs per lane: four
-//    wavefronts per SIMD, two workgroups per CU.
+//    the MFMA.  W4A4: one v_cvt_scalef32_pk_f16_fp4 turns two E2M1 codes
+//    into f16 (its scale operand takes only a power of two) and one
+//    v_pk_mul_f16 applies the E4M3 block scale.  An E2M1 value times an E4M3
+//    value has at most 6 significant bits and lies in [2^-10, 2688], so the
+//    f16 operands are exact and v_mfma_f32_16x16x32_f16 (fp32 accumulation)
+//    forms the same products as a bf16 MFMA would.  W4A16: the codes go to
+//    fp32, take the scale in fp32 and are packed to bf16 (exact as well) for
+//    v_mfma_f32_16x16x32_bf16.  128 VGPRs per lane: four wavefronts per
+//    SIMD, two workgroups per CU.
 //  - the routes' activations (x rows gathered by token for GEMM1, y1 slot rows
-//    for GEMM2; both NVFP4) are decoded the same way once per workgroup into
-//    a double-buffered LDS step that the 8 wavefronts share.
+//    for GEMM2) go once per workgroup into a double-buffered LDS step that
+//    the 8 wavefronts share: W4A4 decodes them to f16 the same way, W4A16
+//    copies the bf16 rows.
 //  - lane (r = lane%16, q = lane/16) of an MFMA holds weight row r of its
 //    16-row n-tile and K [64q, 64q+64) of each step, walked in 8 sub-steps;
 //    the activation rows in LDS hold the same K order, rows 16 bytes longer
 //    than their data so that the operand reads are bank-conflict free.
 //  - workgroups are dealt to the XCDs in runs of consecutive (expert, block)
 //    items, so one expert's activation rows are read from one L2.
-// Requirements (else gemm.hip runs): K (H for GEMM1, I for GEMM2) a multiple
-// of 256; 16-byte aligned code arrays and row strides, 4-byte aligned scales.
+// Requirements (else another kernel runs): K (H for GEMM1, I for GEMM2) a
+// multiple of 256; 16-byte aligned code arrays and row strides, 4-byte
+// aligned scales.
 #include <type_traits>
 
 #include "device_common.h"
@@ -49,12 +56,12 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int NV_THREADS = 512;
-constexpr int NV_RB = 48;                     // route rows per pass (3 MFMA m-tiles)
+constexpr int NV_RB = 48;                     // W4A4: route rows per pass (3 MFMA m-tiles)
+constexpr int NV_RB16 = 32;                   // W4A16: route rows per pass (2 MFMA m-tiles)
 constexpr int NV_NB = 256;                    // weight rows per workgroup (32 per wavefront)
 constexpr int NV_PAIRS = NV_NB / 2;           // GEMM1: gate / up pairs per workgroup
 constexpr int NV_KS = 256;                    // K per step
 constexpr int NV_ROW = NV_KS * 2 + 16;        // LDS row stride of the decoded activations (16 B pad)
-constexpr int NV_BUF = NV_RB * NV_ROW;        // one LDS activation step (33 KiB)
 
 struct NvArgs {
   const uint8_t* A;      // activation codes: x rows (GEMM1, by token) or y1 rows (GEMM2, by slot)
@@ -145,10 +152,15 @@ template <> struct AStep<NV_W4A4> {
   u32x4_t c;
   uint32_t s;
 };
+// W4A16: 16-byte chunks of one bf16 activation step per thread
+constexpr int NV_A16_PER = NV_RB16 * NV_KS * 2 / 16 / NV_THREADS;
 template <> struct AStep<NV_W4A16> {
-  u32x4_t c[3];
+  u32x4_t c[NV_A16_PER];
 };
-constexpr int NV_A16_CHUNKS = NV_RB * NV_KS * 2 / 16;  // 16-byte chunks of one bf16 step (1536)
+// route rows per pass: W4A16 holds its activation step in registers as bf16
+// (twice the bytes of NVFP4) and decodes weights through fp32, so its passes
+// are 32 rows tall to stay within 128 VGPRs without spilling
+template <int MODE> constexpr int nv_rb() { return MODE == NV_W4A16 ? NV_RB16 : NV_RB; }
 
 // AK: the FC1 activation (ACT_*), fixed per instantiation so that the
 // unrolled epilogue carries one kind's code
@@ -156,9 +168,11 @@ template <int MODE, int GEMM, bool ATOMIC, int AK>
 __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArgs a) {
   // MFMA operands: f16 (W4A4, both sides decoded exactly) or bf16 (W4A16)
   using op_t = std::conditional_t<MODE == NV_W4A4, f16x8_t, bf16x8_t>;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2 * NV_BUF];
-  __shared__ int32_t row_src[NV_RB];
-  __shared__ int32_t row_route[NV_RB];
+  constexpr int RB = nv_rb<MODE>();
+  constexpr int BUF = RB * NV_ROW;  // one LDS activation step
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2 * BUF];
+  __shared__ int32_t row_src[RB];
+  __shared__ int32_t row_route[RB];
 
   // (expert, block) item of this workgroup: XCD x (blocks are dealt to the
   // 8 XCDs round-robin) takes items x*per .. x*per + per - 1
@@ -209,10 +223,10 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
   const int ar = tid >> 3, ap = tid & 7;
   const int KT = a.K / NV_KS;
 
-  for (int p0 = 0; p0 < cnt; p0 += NV_RB) {
-    const int valid = min(NV_RB, cnt - p0);
+  for (int p0 = 0; p0 < cnt; p0 += RB) {
+    const int valid = min(RB, cnt - p0);
     __syncthreads();  // the previous pass is done with the LDS steps and row tables
-    if (tid < NV_RB) {
+    if (tid < RB) {
       int route = -1, src = 0;
       if (tid < valid) {
         const int slot = slot_base + p0 + tid;
@@ -228,10 +242,11 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
     // row 0 of A, which exists, and store nothing, so each step issues the
     // same loads on every path.
     //  W4A4: thread (row ar, part ap) decodes K [32 ap, 32 ap + 32) of row ar;
-    //  W4A16: thread tid copies chunks tid, tid + 512, tid + 1024 of the
-    //  step (chunk c: row c / 32, K [8 (c % 32), + 8)).
-    bool a_ok[3];
-    uint32_t aco[3], aso = 0;
+    //  W4A16: thread tid copies chunks tid, tid + 512 of the step (chunk c:
+    //  row c / 32, K [8 (c % 32), + 8)).
+    constexpr int NA = MODE == NV_W4A4 ? 1 : NV_A16_PER;
+    bool a_ok[NA];
+    uint32_t aco[NA], aso = 0;
     if constexpr (MODE == NV_W4A4) {
       a_ok[0] = ar < valid;
       const int asrc = a_ok[0] ? row_src[ar] : 0;
@@ -239,7 +254,7 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
       aso = (uint32_t)asrc * (uint32_t)a.a_sf_row + 2u * ap;
     } else {
 #pragma unroll
-      for (int i = 0; i < 3; i++) {
+      for (int i = 0; i < NA; i++) {
         const int c = tid + NV_THREADS * i, row = c >> 5;
         a_ok[i] = row < valid;
         aco[i] = (uint32_t)(a_ok[i] ? row_src[row] : 0) * (uint32_t)a.a_row_bytes + 16u * (c & 31);
@@ -251,7 +266,7 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
         b.s = *reinterpret_cast<const uint16_t*>(a.A_sf + ou(aso + (uint32_t)s * (NV_KS / 16)));
       } else {
 #pragma unroll
-        for (int i = 0; i < 3; i++)
+        for (int i = 0; i < NA; i++)
           b.c[i] = *reinterpret_cast<const u32x4_t*>(a.A + ou(aco[i] + (uint32_t)s * (NV_KS * 2)));
       }
     };
@@ -260,7 +275,7 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
       if constexpr (MODE == NV_W4A4) {
         if (!a_ok[0]) return;
         const Sc4 sc = e4m3x4_f16(b.s);
-        uint8_t* row = xs + buf * NV_BUF + ar * NV_ROW + 64 * ap;
+        uint8_t* row = xs + buf * BUF + ar * NV_ROW + 64 * ap;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const f16x8_t v = e2m1x8_f16(b.c[j], sc[j >> 1]);
@@ -268,9 +283,9 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 3; i++) {
+        for (int i = 0; i < NA; i++) {
           const int c = tid + NV_THREADS * i;
-          if (a_ok[i]) *reinterpret_cast<u32x4_t*>(xs + buf * NV_BUF + (c >> 5) * NV_ROW + 16 * (c & 31)) = b.c[i];
+          if (a_ok[i]) *reinterpret_cast<u32x4_t*>(xs + buf * BUF + (c >> 5) * NV_ROW + 16 * (c & 31)) = b.c[i];
         }
       }
     };
@@ -285,7 +300,7 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
         for (int n = 0; n < 2; n++) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
       auto compute = [&](const WStep& w, int buf) __attribute__((always_inline)) {
-        const uint8_t* xb = xs + buf * NV_BUF + r * NV_ROW + 128 * q;
+        const uint8_t* xb = xs + buf * BUF + r * NV_ROW + 128 * q;
         Sc4 sc0, sc1;
         if constexpr (MODE == NV_W4A4) {
           sc0 = e4m3x4_f16(w.s[0]);
@@ -473,9 +488,14 @@ __global__ __launch_bounds__(NV_THREADS, 4) void nvfp4_stream_kernel(const NvArg
     };
 
     const int mt = (valid + 15) >> 4;
-    if (mt == 1) run(std::integral_constant<int, 1>{});
-    else if (mt == 2) run(std::integral_constant<int, 2>{});
-    else run(std::integral_constant<int, 3>{});
+    if (mt == 1) {
+      run(std::integral_constant<int, 1>{});
+    } else if constexpr (RB == 32) {
+      run(std::integral_constant<int, 2>{});
+    } else {
+      if (mt == 2) run(std::integral_constant<int, 2>{});
+      else run(std::integral_constant<int, 3>{});
+    }
   }
 }
 
