@@ -330,9 +330,15 @@ void moe_opts_init(moe_opts_t* opts);
  * "vllm.models.flint.ops.moe_cute", grouped_moe, which the page's caller
  * picks per batch).  It estimates the routes per local expert as
  * M * top_k / num_experts (the local share of the routes spread over the
- * local experts) and returns 16 up to 16 routes, 32 up to 48, 64 up to 96,
- * else 128 -- or 256 in the MXFP8_MXFP4 mode above 384 routes, the tile of
- * the large-batch benchmark in FlashInfer pull request 4440. */
+ * local experts) and returns 16 up to 16 routes, then by mode (the
+ * fastest kernel measured at each size):
+ *   W4A16      : 32 up to 32 routes (the expert-streaming kernel), else 128
+ *                (the wide-tile kernel);
+ *   W4A4       : 32 up to 48 routes, else 64 (the expert-streaming kernel
+ *                at every larger size);
+ *   MXFP8_MXFP4: 32 up to 48, 64 up to 96, 128 up to 384, else 256, the
+ *                tile of the large-batch benchmark in FlashInfer pull
+ *                request 4440. */
 int moe_default_tile(int M, int top_k, int num_experts, int num_local_experts, moe_quant_mode_t mode);
 
 /* Bytes of device workspace moe_forward needs: the caller-owned buffers of

@@ -306,11 +306,17 @@ int moe_default_tile(int M, int top_k, int num_experts, int num_local_experts, m
   const int E = num_experts > El ? num_experts : El;
   const double per_expert = (double)M * top_k / E;
   if (per_expert <= 16) return 16;
+  // W4A16: the expert-streaming kernel (32-row passes) while one pass covers
+  // an expert, the wide-tile kernel beyond
+  if (mode == MOE_QUANT_W4A16) return per_expert <= 32 ? 32 : 128;
+  // W4A4: the expert-streaming kernel at every larger size (it stays ahead
+  // of the 128-slot tiles at least to 256 routes per expert)
+  if (mode == MOE_QUANT_W4A4) return per_expert <= 48 ? 32 : 64;
   if (per_expert <= 48) return 32;
   if (per_expert <= 96) return 64;
   // the MX mode's large-batch kernel works on 256-slot tiles (the tile of
   // the large-batch benchmark of pull request 4440)
-  if (mode == MOE_QUANT_MXFP8_MXFP4 && per_expert > 384) return 256;
+  if (per_expert > 384) return 256;
   return 128;
 }
 

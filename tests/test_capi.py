@@ -204,7 +204,11 @@ def test_default_tile_counts_local_routes():
     assert moe.default_tile(1024, 8, 64, 8, 0) == 128        # 128 per expert
     assert moe.default_tile(1024, 8, 512, 8, 0) == 16        # 16 per expert
     assert moe.default_tile(1024, 8, 256, 8, 0) == 32        # 32 per expert
-    assert moe.default_tile(1024, 8, 128, 8, 0) == 64        # 64 per expert
+    assert moe.default_tile(1024, 8, 128, 8, 0) == 128       # 64 per expert: W4A16 goes wide
+    assert moe.default_tile(1024, 8, 128, 8, 2) == 64        # MX at 64 per expert
+    # W4A4 keeps the expert-streaming kernel's tiles at every larger size
+    assert moe.default_tile(1024, 8, 128, 128, 1) == 64      # 64 per expert
+    assert moe.default_tile(8192, 8, 128, 128, 1) == 64      # 512 per expert
 
 
 def test_header_constants_match_binding():
