@@ -161,3 +161,38 @@ def staged_requant_check(p, d, plan, toks, got, name, full=None):
     assert agree >= 0.95, agree
     staged = oracle.finalize(y2, e2p_c, p.topk_weights[stoks], p.H, p.routed_scaling_factor)
     check_close(got[:stoks.size], staged, p.mode, f"{name} from the GPU's own y1")
+
+
+_decode_shape = {}
+
+
+@pytest.mark.parametrize("M,path", [(40, "decode"), (40, "tiled"), (256, "auto"), (2048, "auto")])
+def test_decode_shape_batches(M, path):
+    """The W4A16 decode workload's shape (H = 6144, I = 2048, 32 of 256
+    experts local, top-k 8) at larger batches, where the default tile and the
+    path option hand it to the other kernels: the two-launch decode path and
+    the expert-streaming kernels around their crossover (M = 40), the
+    expert-streaming kernel at tile 16 (M = 256) and the wide-tile kernels
+    (M = 2048).  Every token against the plan-based oracle, the forward's own
+    plan bit for bit."""
+    import dataclasses
+
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, assert_plan_equal, check_close, forward_in_workspace, host, say
+    if M not in _decode_shape:
+        wl = dataclasses.replace(synth.WORKLOADS["w4a16_decode"], M=M)
+        say(f"decode shape M={M}: generating and quantising on the host")
+        _decode_shape[M] = oracle.quantize_problem(synth.make_raw(wl))
+    p = _decode_shape[M]
+    d = DeviceProblem(p)
+    tile = moe.default_tile(p.M, p.top_k, p.num_experts, p.num_local_experts, p.mode)
+    mode = {"auto": moe.PATH_AUTO, "decode": moe.PATH_DECODE, "tiled": moe.PATH_TILED}[path]
+    say(f"decode shape M={M}, tile {tile}, path {path}")
+    out, fplan = forward_in_workspace(d, tile, path=mode)
+    torch.cuda.synchronize()
+    ref_plan = oracle.sort(p.topk_ids, p.num_local_experts, p.local_expert_offset, tile)
+    assert_plan_equal(fplan, ref_plan, f"M={M}: the forward's own plan")
+    full = oracle.forward_plan(p, tile)
+    check_close(host(out, np.uint16), full[4], p.mode, f"decode shape M={M} {path}")
