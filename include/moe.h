@@ -262,7 +262,9 @@ moe_status_t moe_grouped_gemm1_act(moe_quant_mode_t mode, const void* x, const u
  *     fp32 [M, top_k] required; `out` must hold its seed (zeros, or the
  *     previous output when accumulating).
  * w2 packed E2M1 [E_l, H, I/2]; w2_sf E4M3 [E_l, H, I/16] or E8M0
- * [E_l, H, I/32]; w2_alpha fp32 [E_l].  Padding rows of y2 are not written. */
+ * [E_l, H, I/32]; w2_alpha fp32 [E_l].  Padding rows of y2 are not written.
+ * y2 must be 16-byte aligned and out 4-byte aligned (else
+ * MOE_ERR_UNSUPPORTED). */
 moe_status_t moe_grouped_gemm2(moe_quant_mode_t mode, const void* y1, const uint8_t* y1_sf,
                                const moe_plan_t* plan, const uint8_t* w2, const uint8_t* w2_sf,
                                const float* w2_alpha, int H, int I, uint16_t* y2, const float* topk_weights,
@@ -289,7 +291,8 @@ moe_status_t moe_grouped_gemm2_bias(moe_quant_mode_t mode, const void* y1, const
  * with separate fp32 multiplies and adds.  accumulate = 0 overwrites `out`
  * and equals accumulating onto a zero output bit for bit.  A token with no
  * local route gets 0 (or keeps its value when accumulating).  y2 bf16
- * [route_slots, H]; topk_weights fp32 [M, top_k]; out bf16 [M, H]. */
+ * [route_slots, H]; topk_weights fp32 [M, top_k]; out bf16 [M, H].  y2 and
+ * out 16-byte aligned, H a multiple of 8 (else MOE_ERR_UNSUPPORTED). */
 moe_status_t moe_finalize(const uint16_t* y2, const moe_plan_t* plan, const float* topk_weights, int H,
                           float routed_scaling_factor, int accumulate, uint16_t* out, moe_stream_t stream);
 
@@ -369,7 +372,8 @@ moe_status_t moe_forward_plan(moe_plan_t* plan, void* workspace, size_t workspac
  * token_final_scales, w1, w1_sf, w1_alpha, w2, w2_sf, w2_alpha,
  * num_experts, top_k, num_local_experts, local_expert_offset, quant_mode)
  * followed by the output, the shapes, the options and the stream.
- *   out: bf16 [M, H], overwritten (accumulate = 0) or added to.
+ *   out: bf16 [M, H], overwritten (accumulate = 0) or added to; 16-byte
+ *        aligned (else MOE_ERR_UNSUPPORTED).
  * Enqueues moe_sort, moe_grouped_gemm1_swiglu, moe_grouped_gemm2 and (in
  * deterministic mode) moe_finalize; in atomic mode with accumulate = 0 the
  * output is zero-filled first by a kernel.  Decode-sized W4A16 batches
@@ -377,9 +381,11 @@ moe_status_t moe_forward_plan(moe_plan_t* plan, void* workspace, size_t workspac
  * 4-byte aligned w1_sf and w2_sf, and the routing plan plus one bf16 row
  * of H within 64 KiB of LDS; opts->path selects when, see moe_path_t) take
  * two launches
- * instead: GEMM1 with the routing plan, then GEMM2 whose last workgroup per
- * 64 output columns applies the finalize; that finalize is the
- * deterministic one in either mode.
+ * instead: GEMM1 with the routing plan, then GEMM2, which finalizes too:
+ * in deterministic mode the last workgroup per 64 output columns applies
+ * the route-order finalize to them; in atomic mode every route row is
+ * added into out with packed-bf16 atomics (GEMM1 clears out first unless
+ * accumulating).
  * `out` is this GPU's share: the sum over its local routes only. */
 moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk_ids, const float* topk_weights,
                          const uint8_t* w1, const uint8_t* w1_sf, const float* w1_alpha, const uint8_t* w2,

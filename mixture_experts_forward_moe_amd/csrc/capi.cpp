@@ -246,6 +246,8 @@ moe_status_t moe_grouped_gemm2_bias(moe_quant_mode_t mode, const void* y1, const
   if ((mode == MOE_QUANT_W4A16) != (y1_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
   if ((y2 == NULL) == (out == NULL)) return MOE_ERR_INVALID_ARGUMENT;  // exactly one finalize mode
   if (out && !topk_weights) return MOE_ERR_INVALID_ARGUMENT;
+  // packed-bf16 atomics into out; 16-byte stores of y2 rows
+  if ((out && ((uintptr_t)out & 3) != 0) || (y2 && ((uintptr_t)y2 & 15) != 0)) return MOE_ERR_UNSUPPORTED;
   Gemm2Params p = {};
   p.mode = mode;
   p.y1 = y1;
@@ -279,6 +281,7 @@ moe_status_t moe_finalize(const uint16_t* y2, const moe_plan_t* plan, const floa
   if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (plan->M > 0 && (!y2 || !topk_weights || !out)) return MOE_ERR_INVALID_ARGUMENT;
   if (plan->M == 0) return MOE_OK;
+  if (((uintptr_t)y2 & 15) != 0 || ((uintptr_t)out & 15) != 0) return MOE_ERR_UNSUPPORTED;  // 16-byte accesses
   return dev(launch_finalize(y2, plan->expanded_to_permuted, topk_weights, plan->M, plan->top_k, H,
                              routed_scaling_factor, accumulate ? 1 : 0, out, (hipStream_t)stream));
 }
@@ -369,6 +372,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   if (opts->path != MOE_PATH_AUTO && opts->path != MOE_PATH_DECODE && opts->path != MOE_PATH_TILED)
     return MOE_ERR_INVALID_ARGUMENT;
   if (M > 0 && (!x || !topk_ids || !topk_weights || !out)) return MOE_ERR_INVALID_ARGUMENT;
+  if (M > 0 && ((uintptr_t)out & 15) != 0) return MOE_ERR_UNSUPPORTED;  // 16-byte accesses and bf16-pair atomics
   if (!w1 || !w1_sf || !w1_alpha || !w2 || !w2_sf || !w2_alpha) return MOE_ERR_INVALID_ARGUMENT;
   if ((quant_mode == MOE_QUANT_W4A16) != (x_sf == NULL)) return MOE_ERR_INVALID_ARGUMENT;
   if ((quant_mode == MOE_QUANT_W4A4) != (opts->fc2_input_scale != NULL)) return MOE_ERR_INVALID_ARGUMENT;
@@ -398,7 +402,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
   // (the decode kernels read scale pairs as aligned 32-bit words)
   // the decode path streams each expert's weights once per route row: by
   // default it is taken only while the batch is expected to give a local
-  // expert at most 1.5 routes
+  // expert at most 1.25 routes
   const bool dec_wanted = opts->path == MOE_PATH_DECODE ||
                           (opts->path == MOE_PATH_AUTO && 4 * (int64_t)M * top_k <= 5 * (int64_t)num_experts);
   const bool dec = dec_wanted && tile == 16 && decode_supported(quant_mode, M, top_k, num_local_experts, H, I) &&
@@ -440,6 +444,7 @@ moe_status_t moe_forward(const void* x, const uint8_t* x_sf, const int32_t* topk
     d.topk_weights = topk_weights;
     d.routed_scaling_factor = opts->routed_scaling_factor;
     d.accumulate = opts->accumulate;
+    d.atomic = opts->finalize_mode == MOE_FINALIZE_ATOMIC;
     d.out = out;
     d.plan = &plan;
     MarkCtx mc = {ev, st, hipSuccess};

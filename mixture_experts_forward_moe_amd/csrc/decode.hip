@@ -79,6 +79,7 @@ struct DecArgs {
   const float* topk_w;
   float rsf;
   int accumulate;
+  int zero_out;          // GEMM1 clears out (the atomic finalize adds into it)
   uint16_t* out;
   // plan arrays written by dec_gemm1's first workgroup
   int32_t *e2p, *p2e, *tile_expert, *tile_limit, *num_tiles, *offsets, *counts;
@@ -393,6 +394,14 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm1_kernel(const DecArgs a)
   if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int c = threadIdx.x; c < a.H / 64; c += DEC_THREADS)
       __hip_atomic_store(done_count(a, c), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the atomic finalize of GEMM2 adds into out: clear it here, 16 bytes a
+  // thread over the whole grid (out is not read by this launch)
+  if (a.zero_out) {
+    const int64_t n16 = (int64_t)a.M * a.H / 8;
+    const int64_t nthr = (int64_t)gridDim.x * gridDim.y * DEC_THREADS;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * DEC_THREADS + threadIdx.x; i < n16; i += nthr)
+      reinterpret_cast<u32x4_t*>(a.out)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  }
   const int nt = plan_counts(a, P);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rr = lane >> 4, ch = lane & 15;
@@ -618,8 +627,11 @@ constexpr int DEC_YMAX = 4;  // u32x4 per thread for one y1 row: I <= 8192
 // Workgroup (bx, y): y2 columns 64 bx .. 64 bx + 63 of tiles y, y +
 // gridDim.y, ...  Per route row: the y1 row goes into registers, the first
 // D weight steps are issued, then y1 goes to LDS (waiting for its own loads
-// only) and the stream starts.
-template <int D>
+// only) and the stream starts.  ATOMIC: each row's 64 outputs, rounded to
+// bf16 and times the route's weight x routed_scaling_factor, are added into
+// out with packed-bf16 atomics (out cleared by GEMM1 unless accumulating);
+// no y2, no count, no finalize.
+template <int D, bool ATOMIC>
 __global__ __launch_bounds__(DEC_THREADS) void dec_gemm2_kernel(const DecArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t xs[8192 / 2];
   __shared__ uint16_t ybuf[64];
@@ -676,12 +688,26 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_gemm2_kernel(const DecArgs a)
         if (ch == 0) ybuf[16 * wave + 4 * g + rr] = f32_to_bf16(y2v);
       }
       lds_barrier();
-      // the row's 64 outputs: one 128-byte line from 32 lanes
-      if (tid < 32)
-        st_dev(reinterpret_cast<uint32_t*>(a.y2 + (int64_t)(slot0 + r0) * a.H + c0) + tid,
-               reinterpret_cast<const uint32_t*>(ybuf)[tid]);
+      if constexpr (ATOMIC) {
+        if (tid < 32) {
+          const int route = a.p2e[slot0 + r0];
+          const float wf = __fmul_rn(a.topk_w[route], a.rsf);
+          const uint32_t yy = reinterpret_cast<const uint32_t*>(ybuf)[tid];
+          const float v0 = __fmul_rn(wf, __uint_as_float(yy << 16));
+          const float v1 = __fmul_rn(wf, __uint_as_float(yy & 0xffff0000u));
+          bf16x2_t pv = {(__bf16)v0, (__bf16)v1};
+          __builtin_amdgcn_global_atomic_fadd_v2bf16(
+              reinterpret_cast<bf16x2_t*>(a.out + (int64_t)(route / a.top_k) * a.H + c0 + 2 * tid), pv);
+        }
+      } else {
+        // the row's 64 outputs: one 128-byte line from 32 lanes
+        if (tid < 32)
+          st_dev(reinterpret_cast<uint32_t*>(a.y2 + (int64_t)(slot0 + r0) * a.H + c0) + tid,
+                 reinterpret_cast<const uint32_t*>(ybuf)[tid]);
+      }
     }
   }
+  if constexpr (ATOMIC) return;
   const int old = publish_bump(done_count(a, blockIdx.x));
   if (tid == 0) last = (old == (int)gridDim.y - 1);
   __syncthreads();
@@ -729,6 +755,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   a.topk_w = p.topk_weights;
   a.rsf = p.routed_scaling_factor;
   a.accumulate = p.accumulate;
+  a.zero_out = p.atomic && !p.accumulate;
   a.out = p.out;
   a.e2p = p.plan->expanded_to_permuted;
   a.p2e = p.plan->permuted_to_expanded;
@@ -764,7 +791,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.mark) p.mark(p.mark_ctx, 2);
-  dec_gemm2_kernel<4><<<g2, DEC_THREADS, 0, stream>>>(a);  // 4 * I/512 K-steps: a multiple of 4
+  // 4 * I/512 K-steps: a multiple of 4
+  if (p.atomic) dec_gemm2_kernel<4, true><<<g2, DEC_THREADS, 0, stream>>>(a);
+  else dec_gemm2_kernel<4, false><<<g2, DEC_THREADS, 0, stream>>>(a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.mark) p.mark(p.mark_ctx, 3);  // the finalize ran inside GEMM2

@@ -108,6 +108,7 @@ struct DecodeParams {
   const float* topk_weights;
   float routed_scaling_factor;
   int accumulate;
+  int atomic;     // finalize: 0 deterministic (route order, in GEMM2's last workgroups), 1 packed-bf16 atomics
   uint16_t* out;
   const moe_plan_t* plan;
   void (*mark)(void* ctx, int phase);  // optional: called between the launches

@@ -98,6 +98,13 @@ def test_gemm_argument_checks():
     assert g2(0, F, None, p, F, F, F, 256, 512, None, None, 1.0, None, None) == INVALID
     assert g2(0, F, None, p, F, F, F, 256, 512, None, None, 1.0, F, None) == INVALID  # atomic needs weights
     assert L.moe_finalize(F, p, F, 100, 1.0, 0, F, None) == UNSUPPORTED
+    # alignment: y2 rows take 16-byte stores, out packed-bf16 atomics (4 bytes)
+    # and, in the finalize, 16-byte accesses
+    odd2, odd4 = ctypes.c_void_p(0x10002), ctypes.c_void_p(0x10004)
+    assert g2(0, F, None, p, F, F, F, 256, 512, odd4, None, 1.0, None, None) == UNSUPPORTED
+    assert g2(0, F, None, p, F, F, F, 256, 512, None, F, 1.0, odd2, None) == UNSUPPORTED
+    assert L.moe_finalize(odd4, p, F, 256, 1.0, 0, F, None) == UNSUPPORTED
+    assert L.moe_finalize(F, p, F, 256, 1.0, 0, odd4, None) == UNSUPPORTED
 
 
 def test_activation_argument_checks():
@@ -154,6 +161,10 @@ def test_forward_argument_checks():
     o.path = 3
     assert L.moe_forward(*args(0, None)) == INVALID
     o.path = moe.PATH_AUTO
+    # an output that is not 16-byte aligned
+    odd = ctypes.c_void_p(0x10002)
+    assert L.moe_forward(F, None, F, F, F, F, F, F, F, F, 8, 2, 8, 0, 0, odd, 16, 256, 512, ctypes.byref(o),
+                         None) == UNSUPPORTED
     assert L.moe_forward(F, None, F, F, F, F, F, F, F, F, 8, 2, 8, 0, 0, F, 16, 256, 512, None, None) == INVALID
 
 

@@ -377,7 +377,9 @@ def decode_case(case):
 def test_decode_path_edge_cases(case):
     """Decode-sized batches (tile 16) through the two-launch path: no
     local route at all, experts with several tiles and a ragged last tile,
-    a single token, an expert window with a clamped SwiGLU."""
+    a single token, an expert window with a clamped SwiGLU; both finalize
+    modes (the atomic one on an output that starts as garbage), each also
+    accumulating."""
     import torch
 
     import mixture_experts_forward_moe_amd as moe
@@ -390,21 +392,28 @@ def test_decode_path_edge_cases(case):
     out = d.forward(tile=16, path=moe.PATH_DECODE)
     torch.cuda.synchronize()
     want = oracle.forward_tokens(p, np.arange(p.M))
+    out_a = torch.full((p.M, p.H), 0x3f80, dtype=torch.int16, device="cuda")  # garbage the call must clear
+    d.forward(out=out_a, tile=16, path=moe.PATH_DECODE, finalize_mode=moe.FINALIZE_ATOMIC)
+    torch.cuda.synchronize()
     if case == "no_local_routes":
         assert np.all(host(out, np.uint16) == 0) and np.all(want == 0)
+        assert np.all(host(out_a, np.uint16) == 0)
         prev = synth.normal_bf16(3, 3, (p.M, p.H))
-        out = dev(prev.copy())
-        d.forward(out=out, tile=16, path=moe.PATH_DECODE, accumulate=True)
-        torch.cuda.synchronize()
-        assert np.array_equal(host(out, np.uint16), prev)
+        for fm in (moe.FINALIZE_DETERMINISTIC, moe.FINALIZE_ATOMIC):
+            out = dev(prev.copy())
+            d.forward(out=out, tile=16, path=moe.PATH_DECODE, accumulate=True, finalize_mode=fm)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(out, np.uint16), prev)
     else:
         check_close(host(out, np.uint16), want, p.mode, f"decode {case}")
+        check_close(host(out_a, np.uint16), want, p.mode, f"decode {case} atomic")
         prev = synth.normal_bf16(8, 8, (p.M, p.H), 0.0, 0.01)
-        acc = dev(prev.copy())
-        d.forward(out=acc, tile=16, path=moe.PATH_DECODE, accumulate=True)
-        torch.cuda.synchronize()
-        check_close(host(acc, np.uint16), oracle.forward_tokens(p, np.arange(p.M), accumulate=True, out_prev=prev),
-                    p.mode, f"decode {case} accumulate")
+        want_acc = oracle.forward_tokens(p, np.arange(p.M), accumulate=True, out_prev=prev)
+        for fm in (moe.FINALIZE_DETERMINISTIC, moe.FINALIZE_ATOMIC):
+            acc = dev(prev.copy())
+            d.forward(out=acc, tile=16, path=moe.PATH_DECODE, accumulate=True, finalize_mode=fm)
+            torch.cuda.synchronize()
+            check_close(host(acc, np.uint16), want_acc, p.mode, f"decode {case} accumulate (finalize {fm})")
 
 
 DECODE_PLAN_CASES = ["w4a16_decode", "no_local_routes", "hot_experts", "one_token", "offset_swiglu", "relu2"]
