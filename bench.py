@@ -12,7 +12,8 @@ Weights, activations and routing are rotated over several resident copies
 so that no step finds the previous steps' weights in the 256 MB MALL (the
 "cold" figure, the metric); the "warm" figure replays one copy.
 
-Also in the line: per-forward latency percentiles, the measured streaming
+Also in the line: per-forward latency percentiles, the decode forward with
+the atomic finalize, the measured streaming
 copy bandwidth as a second roofline denominator, the routing-locality
 report of the large-batch plan (distinct 2 MiB pages of x per GEMM1 tile)
 and the CPU oracle timed on the host cores.
@@ -170,13 +171,15 @@ def _forwarder(moe, g, wl, out, opts):
     return step
 
 
-def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False, latency: int = 0):
+def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False, latency: int = 0,
+               finalize_mode: int = 0):
     """Times `steps` forwards replayed from a HIP graph that holds `copies`
     forwards, one per resident input copy (no host work between launches).
     HIP events on the replay stream bracket the timed replays.  With
     latency > 0, also per-forward times: one graph per copy, `latency`
     replays rotating over the copies (cold) and on one copy (warm), an event
-    between consecutive replays."""
+    between consecutive replays.  finalize_mode: moe.FINALIZE_* of the
+    forwards."""
     import torch
 
     import mixture_experts_forward_moe_amd as moe
@@ -186,7 +189,7 @@ def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False, l
     ws = torch.empty(moe.workspace_size(wl.M, H, I, wl.top_k, E, tile, wl.mode), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.M, H), dtype=torch.int16, device="cuda")
     skw = _scale_kw(g, scaled)
-    opts = _opts(moe, wl, ws, tile, fc2=g.fc2, **skw)
+    opts = _opts(moe, wl, ws, tile, fc2=g.fc2, finalize_mode=finalize_mode, **skw)
     step = _forwarder(moe, g, wl, out, opts)
 
     for i in range(max(warmup, copies)):  # eager warm-up (also caches the launch shape)
@@ -237,7 +240,8 @@ def time_graph(wl, steps: int, warmup: int, copies: int, scaled: bool = False, l
     return res
 
 
-def time_phases(wl, steps: int, warmup: int, copies: int, scaled: bool = False, plan_out: dict | None = None):
+def time_phases(wl, steps: int, warmup: int, copies: int, scaled: bool = False, plan_out: dict | None = None,
+                finalize_mode: int = 0):
     """Times `steps` eager forwards, then the same steps again with HIP
     events that moe_forward records between its launches on the same
     stream (per-kernel durations, and per-step forward times for the
@@ -257,8 +261,9 @@ def time_phases(wl, steps: int, warmup: int, copies: int, scaled: bool = False, 
             e.record()
     torch.cuda.synchronize()
     skw = _scale_kw(g, scaled)
-    opts = _opts(moe, wl, ws, tile, fc2=g.fc2, **skw)
-    opts_ev = [_opts(moe, wl, ws, tile, fc2=g.fc2, phase_events=events[i], **skw) for i in range(steps)]
+    opts = _opts(moe, wl, ws, tile, fc2=g.fc2, finalize_mode=finalize_mode, **skw)
+    opts_ev = [_opts(moe, wl, ws, tile, fc2=g.fc2, phase_events=events[i], finalize_mode=finalize_mode, **skw)
+               for i in range(steps)]
     step = _forwarder(moe, g, wl, out, opts)
 
     for i in range(warmup):
@@ -606,6 +611,17 @@ def main():
         "weights": {"bytes": by["weights"], "GBps": w_gbs, "hbm_frac": w_gbs / HBM_PEAK_GBS,
                     "copy_frac": w_gbs / copy_gbs, "tflops": fl / (f_ms * 1e-3) / 1e12},
     }
+    # the same decode forward with the atomic (fused) finalize: GEMM2 adds its
+    # rows into out with packed-bf16 atomics instead of the route-order
+    # finalize (faster at decode sizes, not reproducible bit for bit)
+    log(f"bench: {wl.name}: {args.steps} steps with the atomic finalize (graph replay)")
+    ra = time_graph(wl, args.steps, args.warmup, args.copies, finalize_mode=1)
+    fa_gbs = by["forward"] / (ra["gpu_ms_per_step"] * 1e-3) / 1e9
+    line["finalize_atomic"] = {"tokens_per_s": wl.M * ra["steps"] / ra["seconds"],
+                               "ms_per_forward": ra["gpu_ms_per_step"], "GBps": fa_gbs,
+                               "hbm_frac": fa_gbs / HBM_PEAK_GBS, "copy_frac": fa_gbs / copy_gbs,
+                               "note": "decode forward with finalize_mode ATOMIC (packed-bf16 atomics from "
+                                       "GEMM2); the headline uses the deterministic finalize"}
     if not args.no_secondary:
         wl2 = synth.WORKLOADS["w4a16_prefill"]
         steps2 = max(20, args.steps // 10)
