@@ -520,6 +520,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-atomic", action="store_true", help="skip the decode forward with the atomic finalize")
     ap.add_argument("--workload", default="w4a16_decode")
     ap.add_argument("--only", choices=["prefill", "w4a4", "mx"], default=None,
                     help="profiling aid: time only this secondary workload (no headline line)")
@@ -614,14 +615,15 @@ def main():
     # the same decode forward with the atomic (fused) finalize: GEMM2 adds its
     # rows into out with packed-bf16 atomics instead of the route-order
     # finalize (faster at decode sizes, not reproducible bit for bit)
-    log(f"bench: {wl.name}: {args.steps} steps with the atomic finalize (graph replay)")
-    ra = time_graph(wl, args.steps, args.warmup, args.copies, finalize_mode=1)
-    fa_gbs = by["forward"] / (ra["gpu_ms_per_step"] * 1e-3) / 1e9
-    line["finalize_atomic"] = {"tokens_per_s": wl.M * ra["steps"] / ra["seconds"],
-                               "ms_per_forward": ra["gpu_ms_per_step"], "GBps": fa_gbs,
-                               "hbm_frac": fa_gbs / HBM_PEAK_GBS, "copy_frac": fa_gbs / copy_gbs,
-                               "note": "decode forward with finalize_mode ATOMIC (packed-bf16 atomics from "
-                                       "GEMM2); the headline uses the deterministic finalize"}
+    if not args.no_atomic:
+        log(f"bench: {wl.name}: {args.steps} steps with the atomic finalize (graph replay)")
+        ra = time_graph(wl, args.steps, args.warmup, args.copies, finalize_mode=1)
+        fa_gbs = by["forward"] / (ra["gpu_ms_per_step"] * 1e-3) / 1e9
+        line["finalize_atomic"] = {"tokens_per_s": wl.M * ra["steps"] / ra["seconds"],
+                                   "ms_per_forward": ra["gpu_ms_per_step"], "GBps": fa_gbs,
+                                   "hbm_frac": fa_gbs / HBM_PEAK_GBS, "copy_frac": fa_gbs / copy_gbs,
+                                   "note": "decode forward with finalize_mode ATOMIC (packed-bf16 atomics from "
+                                           "GEMM2); the headline uses the deterministic finalize"}
     if not args.no_secondary:
         wl2 = synth.WORKLOADS["w4a16_prefill"]
         steps2 = max(20, args.steps // 10)
