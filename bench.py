@@ -12,8 +12,13 @@ Weights, activations and routing are rotated over several resident copies
 so that no step finds the previous steps' weights in the 256 MB MALL (the
 "cold" figure, the metric); the "warm" figure replays one copy.
 
-Also in the line: per-forward latency percentiles, the decode forward with
-the atomic finalize, the measured streaming
+The headline decode forward uses the fused finalize (GEMM2 adds each
+route's scaled rows into the output with packed-bf16 atomics), the
+default of the pages' API ("flashinfer.fused_moe.cute_dsl_fused_moe",
+Parameters: use_fused_finalize); the same forward with the deterministic
+route-order finalize is reported beside it.
+
+Also in the line: per-forward latency percentiles, the measured streaming
 copy bandwidth as a second roofline denominator, the routing-locality
 report of the large-batch plan (distinct 2 MiB pages of x per GEMM1 tile)
 and the CPU oracle timed on the host cores.
@@ -296,19 +301,21 @@ def time_phases(wl, steps: int, warmup: int, copies: int, scaled: bool = False, 
 
 
 # ------------------------------------------------------------------ algorithmic work
-def w4a16_bytes(wl, routes, active):
+def w4a16_bytes(wl, routes, active, atomic: bool = False):
     """Algorithmic HBM bytes: active experts' NVFP4 weights (codes + E4M3
     block scales); per local route its token's bf16 row read, y1 written and
-    read, y2 written and read; routing ids and weights read; the output
-    written once."""
+    read, and y2 written and read (deterministic finalize) or its row added
+    into the output once (atomic finalize, after GEMM1 has zeroed the
+    output); routing ids and weights read; the output written once."""
     H, I = wl.H, wl.I
     R1 = I if wl.activation == 2 else 2 * I   # W1 rows: ReLU^2 is non-gated
     w1 = R1 * H // 2 + R1 * H // 16
     w2 = H * I // 2 + H * I // 16
-    act = routes * (2 * H + 2 * 2 * I + 2 * 2 * H)
+    y2 = 2 * H if atomic else 2 * 2 * H
+    act = routes * (2 * H + 2 * 2 * I + y2)
     io = wl.M * wl.top_k * 8 + wl.M * H * 2
     return dict(
-        gemm1=active * w1 + routes * (H * 2 + I * 2),
+        gemm1=active * w1 + routes * (H * 2 + I * 2) + (wl.M * H * 2 if atomic else 0),
         gemm2=active * w2 + routes * (I * 2 + H * 2),
         forward=active * (w1 + w2) + act + io,
         weights=active * (w1 + w2),
@@ -330,16 +337,19 @@ def flops(wl, routes):
 
 
 # ------------------------------------------------------------------ measured traffic
-def counter_traffic(kernel: str, workload: str):
+def counter_traffic(kernel: str, workload: str, finalize: str | None = None):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE record of this kernel and workload, scaled by the copy
-    calibration; None when there is no record or the kernel source has
-    changed since the counters were taken."""
+    WRITE_SIZE record of this kernel and workload (and finalize mode, where
+    the record names one), scaled by the copy calibration; None when there
+    is no record, it was taken in another finalize mode, or the kernel
+    source has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if finalize is not None and rec.get("finalize", "deterministic") != finalize:
+        return None
     src = os.path.join(ROOT, rec["source"])
     if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
         return None
@@ -520,7 +530,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--no-atomic", action="store_true", help="skip the decode forward with the atomic finalize")
+    ap.add_argument("--finalize", choices=["atomic", "deterministic"], default="atomic",
+                    help="finalize of the headline decode forward (atomic: the pages' default)")
+    ap.add_argument("--no-other-finalize", action="store_true",
+                    help="skip the decode forward with the other finalize (for counter runs)")
     ap.add_argument("--workload", default="w4a16_decode")
     ap.add_argument("--only", choices=["prefill", "w4a4", "mx"], default=None,
                     help="profiling aid: time only this secondary workload (no headline line)")
@@ -557,20 +570,23 @@ def main():
     copy_gbs = cbw["GBps"]
     log(f"bench: {wl.name}: {args.steps} steps after {args.warmup} warm-up (graph replay), then "
         f"{args.latency_samples} forwards one by one")
-    r = time_graph(wl, args.steps, args.warmup, args.copies, latency=args.latency_samples)
+    fmode = moe.FINALIZE_ATOMIC if args.finalize == "atomic" else moe.FINALIZE_DETERMINISTIC
+    atomic = fmode == moe.FINALIZE_ATOMIC
+    r = time_graph(wl, args.steps, args.warmup, args.copies, latency=args.latency_samples, finalize_mode=fmode)
     routes, active = r["local_routes"], r["active_experts"]
-    by = w4a16_bytes(wl, routes, active)
+    by = w4a16_bytes(wl, routes, active, atomic=atomic)
     fl = flops(wl, routes)
     tokens_s = wl.M * r["steps"] / r["seconds"]
     # The decode forward is two launches (dec_gemm1_kernel with the routing
-    # plan, dec_gemm2_kernel with the finalize) replayed back to back from a
+    # plan, dec_gemm2_kernel with the finalize: packed-bf16 atomics into the
+    # output, or the route-order sums of its last workgroups) replayed back to back from a
     # HIP graph; the roofline takes the pair as its unit: algorithmic bytes
     # of the forward over the forward's time from HIP events around the
     # replays.  Per-kernel times come from eager steps with HIP events
     # recorded between the two launches (they include the event's own
     # dispatch gap, a few microseconds per kernel).
     log(f"bench: {wl.name}: {args.steps} eager steps with per-kernel events")
-    rk = time_phases(wl, args.steps, args.warmup, args.copies)
+    rk = time_phases(wl, args.steps, args.warmup, args.copies, finalize_mode=fmode)
     k1_ms, k2_ms = rk["phase_ms"]["gemm1"], rk["phase_ms"]["gemm2"]
     f_ms = r["gpu_ms_per_step"]
     f_gbs = by["forward"] / (f_ms * 1e-3) / 1e9
@@ -590,11 +606,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "quant_mode": "w4a16 (NVFP4 weights, bf16 activations)", "M": wl.M,
                    "H": wl.H, "I": wl.I, "num_experts": wl.num_experts, "num_local_experts": wl.num_local_experts,
-                   "top_k": wl.top_k, "tile": r["tile"], "finalize": "deterministic", "local_routes": routes,
+                   "top_k": wl.top_k, "tile": r["tile"], "finalize": args.finalize, "local_routes": routes,
                    "active_local_experts": active, "resident_copies": args.copies, "launch": "hip graph replay"},
-        "roofline": {"bound": "hbm", "kernel": "dec_gemm1_kernel + dec_gemm2_kernel (one decode forward)",
+        "roofline": {"bound": "hbm", "kernel": f"dec_gemm1_kernel + dec_gemm2_kernel<4, {str(atomic).lower()}> "
+                                               "(one decode forward)",
                      "achieved": f_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": f_gbs / HBM_PEAK_GBS,
-                     "traffic": counter_traffic("dec_forward", wl.name),
+                     "traffic": counter_traffic("dec_forward", wl.name, args.finalize),
                      "algorithmic_bytes": by["forward"], "avg_ms": f_ms,
                      "copy_GBps": copy_gbs, "frac_of_copy": f_gbs / copy_gbs},
         "latency": {"cold": r["cold"], "warm": r["warm"],
@@ -607,23 +624,27 @@ def main():
                                          "GBps": by["gemm1"] / (k1_ms * 1e-3) / 1e9},
                     "dec_gemm2_kernel": {"avg_ms": k2_ms, "algorithmic_bytes": by["gemm2"],
                                          "GBps": by["gemm2"] / (k2_ms * 1e-3) / 1e9,
-                                         "note": "includes the route-order finalize of its last workgroups"},
+                                         "note": "includes the finalize: packed-bf16 atomics into out" if atomic
+                                         else "includes the route-order finalize of its last workgroups"},
                     "timing": "eager steps, HIP events between the launches"},
         "weights": {"bytes": by["weights"], "GBps": w_gbs, "hbm_frac": w_gbs / HBM_PEAK_GBS,
                     "copy_frac": w_gbs / copy_gbs, "tflops": fl / (f_ms * 1e-3) / 1e12},
     }
-    # the same decode forward with the atomic (fused) finalize: GEMM2 adds its
-    # rows into out with packed-bf16 atomics instead of the route-order
-    # finalize (faster at decode sizes, not reproducible bit for bit)
-    if not args.no_atomic:
-        log(f"bench: {wl.name}: {args.steps} steps with the atomic finalize (graph replay)")
-        ra = time_graph(wl, args.steps, args.warmup, args.copies, finalize_mode=1)
-        fa_gbs = by["forward"] / (ra["gpu_ms_per_step"] * 1e-3) / 1e9
-        line["finalize_atomic"] = {"tokens_per_s": wl.M * ra["steps"] / ra["seconds"],
-                                   "ms_per_forward": ra["gpu_ms_per_step"], "GBps": fa_gbs,
-                                   "hbm_frac": fa_gbs / HBM_PEAK_GBS, "copy_frac": fa_gbs / copy_gbs,
-                                   "note": "decode forward with finalize_mode ATOMIC (packed-bf16 atomics from "
-                                           "GEMM2); the headline uses the deterministic finalize"}
+    # the same decode forward with the other finalize: the deterministic
+    # route-order sums (reproducible bit for bit) beside the atomic headline,
+    # or the other way round
+    if not args.no_other_finalize:
+        other = "deterministic" if atomic else "atomic"
+        log(f"bench: {wl.name}: {args.steps} steps with the {other} finalize (graph replay)")
+        ro = time_graph(wl, args.steps, args.warmup, args.copies,
+                        finalize_mode=moe.FINALIZE_DETERMINISTIC if atomic else moe.FINALIZE_ATOMIC)
+        bo = w4a16_bytes(wl, routes, active, atomic=not atomic)["forward"]
+        fo_gbs = bo / (ro["gpu_ms_per_step"] * 1e-3) / 1e9
+        line["finalize_" + other] = {"tokens_per_s": wl.M * ro["steps"] / ro["seconds"],
+                                     "ms_per_forward": ro["gpu_ms_per_step"], "GBps": fo_gbs,
+                                     "hbm_frac": fo_gbs / HBM_PEAK_GBS, "copy_frac": fo_gbs / copy_gbs,
+                                     "note": f"decode forward with the {other} finalize; the headline uses the "
+                                             f"{args.finalize} one"}
     if not args.no_secondary:
         wl2 = synth.WORKLOADS["w4a16_prefill"]
         steps2 = max(20, args.steps // 10)
@@ -655,8 +676,9 @@ def main():
             scaled = name == "swiglu_scaled"
             wd = dataclasses.replace(wl, **kw)
             log(f"bench: {wd.name} with {name}: {max(20, args.steps // 4)} steps (graph replay)")
-            rd = time_graph(wd, max(20, args.steps // 4), max(4, args.warmup // 4), args.copies, scaled=scaled)
-            fd = w4a16_bytes(wd, routes, active)["forward"] / (rd["gpu_ms_per_step"] * 1e-3) / 1e9
+            rd = time_graph(wd, max(20, args.steps // 4), max(4, args.warmup // 4), args.copies, scaled=scaled,
+                            finalize_mode=fmode)
+            fd = w4a16_bytes(wd, routes, active, atomic=atomic)["forward"] / (rd["gpu_ms_per_step"] * 1e-3) / 1e9
             wp = dataclasses.replace(synth.WORKLOADS["w4a16_prefill"], swiglu_limit=float(np.finfo(np.float32).max),
                                      **kw)
             rp = time_phases(wp, 10, 3, args.copies, scaled=scaled)

@@ -1,6 +1,7 @@
 """The five workloads at full size on the GPU against the oracle, in the
-launch configuration the benchmark times (default tile, deterministic
-finalize), plus the atomic finalize:
+launch configuration the benchmark times (default tile), with both the
+deterministic and the atomic finalize (the decode headline times the
+atomic one, the other workloads the deterministic one):
 
   * the routing plan the forward itself built and used (read back from its
     workspace), all seven arrays bit for bit, and the same for a separate
