@@ -301,6 +301,62 @@ def test_mx_wide_tile_many_items():
     check_close(host(out_a, np.uint16)[toks], want, p.mode, "many items atomic")
 
 
+TILED_EDGE_CASES = ["no_local_routes", "one_expert_top1", "two_hot_experts"]
+
+
+def tiled_edge_problem(mode, case):
+    """Routing edge cases at a shape every tiled kernel takes (H = I = 1024:
+    the expert-streaming kernels at tiles up to 64, the 128-slot W4A16 kernel,
+    the MX 256-slot ring kernels)."""
+    key = ("tiled_edge", mode, case)
+    if key in _cache:
+        return _cache[key]
+    if case == "no_local_routes":
+        # no route of the batch falls in the local window: the output is zero
+        wl = synth.small_workload(mode, 96, 1024, 1024, 16, 4, 3, 101, offset=4)
+        raw = synth.make_raw(wl)
+        raw.topk_ids[:] = np.where((raw.topk_ids >= 4) & (raw.topk_ids < 8), raw.topk_ids + 8, raw.topk_ids)
+    elif case == "one_expert_top1":
+        # a single (local) expert and top_k 1: 300 routes, two full 128-slot tiles and a ragged one
+        wl = synth.small_workload(mode, 300, 1024, 1024, 1, 1, 1, 102)
+        raw = synth.make_raw(wl)
+    else:
+        # every token routes to the same two of eight local experts
+        wl = synth.small_workload(mode, 200, 1024, 1024, 8, 8, 2, 103)
+        raw = synth.make_raw(wl)
+        raw.topk_ids[:, 0] = 3
+        raw.topk_ids[:, 1] = 6
+    _cache[key] = oracle.quantize_problem(raw)
+    return _cache[key]
+
+
+@pytest.mark.parametrize("mode", [oracle.W4A16, oracle.W4A4, oracle.MXFP8_MXFP4])
+@pytest.mark.parametrize("case", TILED_EDGE_CASES)
+def test_tiled_path_routing_edge_cases(mode, case):
+    """The tiled forward (sort, GEMM1, GEMM2, finalize) on routing edge cases,
+    at the default tile and at tiles 32, 128 and 256, with both finalize
+    modes (the atomic one onto a garbage-filled output), against the
+    per-token oracle on every token."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, check_close, host, say
+    p = tiled_edge_problem(mode, case)
+    d = DeviceProblem(p)
+    want = oracle.forward_tokens(p, np.arange(p.M))
+    if case == "no_local_routes":
+        assert not np.any(synth.bf16_to_f32(want)), "the oracle's output is zero"
+    for tile in (0, 32, 128, 256):
+        say(f"tiled edge case {case} mode={mode} tile={tile}")
+        out = d.forward(tile=tile, path=moe.PATH_TILED)
+        torch.cuda.synchronize()
+        check_close(host(out, np.uint16), want, p.mode, f"{case} mode={mode} tile={tile}")
+        out_a = torch.full((p.M, p.H), 0x7fc0, dtype=torch.int16, device="cuda")
+        d.forward(out=out_a, tile=tile, path=moe.PATH_TILED, finalize_mode=moe.FINALIZE_ATOMIC)
+        torch.cuda.synchronize()
+        check_close(host(out_a, np.uint16), want, p.mode, f"{case} mode={mode} tile={tile} atomic")
+
+
 @pytest.mark.parametrize("extra,tile", [(64, 0), (8, 32), (64, 128), (4, 32)])
 def test_row_strided_x(extra, tile):
     """bf16 x rows `extra` elements apart beyond H (the expert-streaming
