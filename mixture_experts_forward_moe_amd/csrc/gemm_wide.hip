@@ -41,7 +41,10 @@
 //  - tile order: heaviest tiles first (by used height), so that the short
 //    tiles fill the tail; each XCD (block b runs on XCD b & 7) takes a fixed
 //    eighth of the weight-row blocks of every tile, so an expert's weights
-//    are read by one XCD and the load is the same on all eight.
+//    are read by one XCD and the load is the same on all eight.  This is the
+//    eight-domain form of the localized weights of
+//    "flashinfer.fused_moe.cute_dsl_fused_moe" (Parameters: FC1 split by I,
+//    FC2 by H, each locality domain reading only its part).
 #include "device_common.h"
 #include "internal.h"
 #include "tile_order.h"
