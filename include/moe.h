@@ -72,8 +72,11 @@ typedef enum { MOE_QUANT_W4A16 = 0, MOE_QUANT_W4A4 = 1, MOE_QUANT_MXFP8_MXFP4 = 
  *                 routes in route order (bitwise reproducible).
  *  ATOMIC       : the GEMM2 epilogue adds w * routed_scaling_factor * y2
  *                 into `out` with packed-bf16 atomics (not reproducible
- *                 bit for bit; no y2 buffer).  Faster at decode sizes;
- *                 at large batches the atomics contend and it is slower. */
+ *                 bit for bit, and each add rounds to bf16; no y2 buffer).
+ *                 The default of the pages' API (use_fused_finalize);
+ *                 here DETERMINISTIC is the default, the zero value.
+ *                 Faster at decode sizes; at large batches the atomics
+ *                 contend and it is slower. */
 typedef enum { MOE_FINALIZE_DETERMINISTIC = 0, MOE_FINALIZE_ATOMIC = 1 } moe_finalize_mode_t;
 
 /* How moe_sort parallelises.  Both give the identical plan.
