@@ -585,3 +585,44 @@ def test_decode_path_graph_replay():
         other = e.forward(tile=16, path=moe.PATH_DECODE, workspace=ws)  # eager work on the same workspace between replays
         torch.cuda.synchronize()
         assert torch.equal(other, want_q), rep
+
+
+@pytest.mark.parametrize("name,tile", [("w4a16_tall", 128), ("w4a4_stream", 32), ("mx_k1024", 256)])
+def test_tiled_path_graph_replay(name, tile):
+    """The tiled forward (sort, GEMM1, GEMM2, finalize or zero fill + atomic
+    GEMM2) captured in a HIP graph: every replay, with an eager forward of
+    another problem on the same workspace in between, gives the eager
+    result (bit for bit with the deterministic finalize; within the bar
+    with the atomic one, whose add order varies).  No step records a
+    memset node."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, check_close, host, say
+    p = problem(name)
+    q = problem("w4a16_tall" if name != "w4a16_tall" else "w4a16_wide")
+    d, e = DeviceProblem(p), DeviceProblem(q)
+    for fm in (moe.FINALIZE_DETERMINISTIC, moe.FINALIZE_ATOMIC):
+        say(f"tiled graph replay {name} tile={tile} finalize={fm}")
+        n = max(moe.workspace_size(r.M, r.H, r.I, r.top_k, r.num_local_experts, tile, r.mode, fm) for r in (p, q))
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        want = d.forward(tile=tile, workspace=ws, finalize_mode=fm)
+        want_q = e.forward(tile=tile, workspace=ws, finalize_mode=fm)
+        torch.cuda.synchronize()
+        out = torch.zeros_like(want)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            d.forward(out=out, tile=tile, workspace=ws, finalize_mode=fm)
+        for rep in range(4):
+            out.fill_(0x7fc0)
+            graph.replay()
+            torch.cuda.synchronize()
+            if fm == moe.FINALIZE_DETERMINISTIC:
+                assert torch.equal(out, want), (name, rep)
+            else:
+                check_close(host(out, np.uint16), host(want, np.uint16), p.mode, f"{name} graph replay {rep}")
+            other = e.forward(tile=tile, workspace=ws, finalize_mode=fm)  # eager work between replays
+            torch.cuda.synchronize()
+            if fm == moe.FINALIZE_DETERMINISTIC:
+                assert torch.equal(other, want_q), (name, rep)
+        del graph
