@@ -626,3 +626,26 @@ def test_tiled_path_graph_replay(name, tile):
             if fm == moe.FINALIZE_DETERMINISTIC:
                 assert torch.equal(other, want_q), (name, rep)
         del graph
+
+
+@pytest.mark.parametrize("name,tile", [("decode", 16), ("w4a16_tall", 128), ("w4a4_stream", 32), ("mx_k1024", 256)])
+def test_forward_on_a_side_stream(name, tile):
+    """Every launch of a forward goes to the caller's stream: the forward on
+    a second stream (default priority) gives the default stream's result bit
+    for bit (deterministic finalize), and its output is complete once that
+    stream alone is synchronized."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, say
+    p = decode_case("offset_swiglu") if name == "decode" else problem(name)
+    d = DeviceProblem(p)
+    say(f"side stream {name} tile={tile}")
+    want = d.forward(tile=tile)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        out = torch.full_like(want, 0x7fc0)
+        d.forward(out=out, tile=tile)
+    side.synchronize()
+    assert torch.equal(out, want), name
