@@ -649,3 +649,36 @@ def test_forward_on_a_side_stream(name, tile):
         d.forward(out=out, tile=tile)
     side.synchronize()
     assert torch.equal(out, want), name
+
+
+def test_concurrent_forwards_on_two_streams():
+    """Two forwards in flight at once on two streams, each with its own
+    workspace (a decode-sized batch and a 128-slot tiled one, then two
+    decode-sized ones): each equals its result run alone.  The library holds
+    no device state across calls besides the caller's workspace."""
+    import torch
+
+    import mixture_experts_forward_moe_amd as moe
+    from gpu_util import DeviceProblem, say
+    pairs = [((decode_case("offset_swiglu"), 16), (problem("w4a16_tall"), 128)),
+             ((decode_case("offset_swiglu"), 16), (decode_case("one_token"), 16))]
+    for (p, tp), (q, tq) in pairs:
+        say(f"two streams: M={p.M} tile={tp} and M={q.M} tile={tq}")
+        d, e = DeviceProblem(p), DeviceProblem(q)
+        want_p = d.forward(tile=tp)
+        want_q = e.forward(tile=tq)
+        torch.cuda.synchronize()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        outs = []
+        for rep in range(3):
+            with torch.cuda.stream(s1):
+                a = torch.full_like(want_p, 0x7fc0)
+                d.forward(out=a, tile=tp)
+            with torch.cuda.stream(s2):
+                b = torch.full_like(want_q, 0x7fc0)
+                e.forward(out=b, tile=tq)
+            outs.append((a, b))
+        torch.cuda.synchronize()
+        for a, b in outs:
+            assert torch.equal(a, want_p)
+            assert torch.equal(b, want_q)
